@@ -1,0 +1,190 @@
+"""Plain CPU definitions of MoE token dispatch and combine (test infrastructure only).
+
+What the pages say the two operators do:
+  * "Inside the Nebius + PyTorch DeepSeek V3 recipe", section "Mixture-of-experts
+    and wide expert parallelism": every MoE layer has a dispatch phase that
+    sends each token to the experts the router picked for it, and a combine
+    phase that brings the expert outputs back to the tokens' original
+    positions.
+  * Hybrid-EP news item, sections "Technical Structure" and "Availability and
+    Integration": the two operators are dispatch and combine, and buffers are
+    preallocated for the worst case because routing is dynamic.
+  * "MoE / Hybrid-EP Validation", "Communication path comparison" and "FP8
+    dispatch restriction": dispatch may carry FP8 payloads; the measured shape
+    is hidden 7168, 4096 tokens per rank, top-8, EP=8.
+
+The pages fix no formula, buffer layout or ordering, so this module writes out
+the plainest reading (each reading is listed in the design notes):
+  * Layout: a stable counting sort of the T*k (token, slot) pairs by expert id.
+    Position = start of the expert's region + number of earlier pairs (token
+    order, then slot order) routed to the same expert. Experts are split into
+    R virtual ranks contiguously, so rank r's rows are one contiguous slab.
+    Ids outside [0, E) are skipped: no row, pos = -1, counted as invalid.
+  * Capacity is the worst case, T*k rows; rows past the valid total keep
+    src_idx = -1.
+  * bf16 dispatch copies each token row, bit for bit, to each of its k rows.
+  * FP8 dispatch quantises each token once, per block of 128 channels:
+    amax = max |x|, scale = amax / 448 in fp32 (correctly rounded), and each
+    code = E4M3 nearest-even of the fp32 quotient x / scale; a block with
+    amax = 0 gets scale 0 and signed-zero codes. Codes and the scale are
+    written to every destination row of the token.
+  * Combine: out[t] = bf16( sum_j w[t,j] * y[pos[t,j]] ), the sum taken over
+    valid slots. The oracle forms it in fp64 (each product is exact there) and
+    rounds once to bf16.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import bf16_decode, bf16_encode, e4m3_decode, e4m3_encode
+
+__all__ = ["layout", "dispatch_bf16", "dispatch_fp8", "combine", "dequant_fp8",
+           "FP8_BLOCK", "FP8_MAX"]
+
+FP8_BLOCK = 128
+FP8_MAX = np.float32(448.0)
+
+
+def layout(topk_idx, num_experts: int, num_ranks: int) -> dict:
+    """Histogram, exclusive scan and stable placement of the routed slots.
+
+    Returns int64 numpy arrays:
+      counts_e [E], offsets_e [E+1], counts_r [R], offsets_r [R+1],
+      pos [T, k] (row of slot (t, j), or -1), src_idx [T*k] (token of each row,
+      -1 past the valid total), and the int ``invalid`` (slots with ids outside
+      [0, E)).
+    """
+    idx = np.asarray(topk_idx)
+    T, k = idx.shape
+    E, R = int(num_experts), int(num_ranks)
+    if E <= 0 or R <= 0 or E % R != 0:
+        raise ValueError("num_experts must be a positive multiple of num_ranks")
+    rows = idx.tolist()
+
+    # Histogram over all slots.
+    counts_e = [0] * E
+    for t in range(T):
+        for j in range(k):
+            e = rows[t][j]
+            if 0 <= e < E:
+                counts_e[e] += 1
+
+    # Exclusive scan over experts; ranks own contiguous groups of E/R experts.
+    offsets_e = [0] * (E + 1)
+    for e in range(E):
+        offsets_e[e + 1] = offsets_e[e] + counts_e[e]
+    per = E // R
+    counts_r = [sum(counts_e[r * per:(r + 1) * per]) for r in range(R)]
+    offsets_r = [offsets_e[r * per] for r in range(R)] + [offsets_e[E]]
+
+    # Stable placement: walk slots in (token, slot) order, one cursor per expert.
+    cursor = offsets_e[:E]
+    pos = [[-1] * k for _ in range(T)]
+    src_idx = [-1] * (T * k)
+    for t in range(T):
+        for j in range(k):
+            e = rows[t][j]
+            if 0 <= e < E:
+                p = cursor[e]
+                cursor[e] = p + 1
+                pos[t][j] = p
+                src_idx[p] = t
+
+    as64 = lambda a: np.asarray(a, dtype=np.int64)  # noqa: E731
+    return {
+        "counts_e": as64(counts_e), "offsets_e": as64(offsets_e),
+        "counts_r": as64(counts_r), "offsets_r": as64(offsets_r),
+        "pos": as64(pos).reshape(T, k), "src_idx": as64(src_idx),
+        "invalid": T * k - offsets_e[E],
+    }
+
+
+def _scatter_rows(rows_per_token: np.ndarray, pos: np.ndarray, capacity: int, fill):
+    """out[pos[t, j]] = rows_per_token[t] for every valid slot; other rows = fill."""
+    T, k = pos.shape
+    out = np.full((capacity,) + rows_per_token.shape[1:], fill, dtype=rows_per_token.dtype)
+    flat = pos.reshape(-1)
+    tok = np.repeat(np.arange(T), k)
+    ok = flat >= 0
+    out[flat[ok]] = rows_per_token[tok[ok]]
+    return out
+
+
+def dispatch_bf16(x_bits, pos) -> np.ndarray:
+    """Copy token rows (bf16 bit patterns, uint16 [T, H]) to their T*k rows."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    pos = np.asarray(pos)
+    T, k = pos.shape
+    return _scatter_rows(x_bits, pos, T * k, 0)
+
+
+def quantize_fp8_rows(x_bits):
+    """Per-token FP8 E4M3 quantisation with one fp32 scale per 128 channels.
+
+    Returns (codes uint8 [T, H], scales float32 [T, H/128]).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, H = x_bits.shape
+    if H % FP8_BLOCK != 0:
+        raise ValueError("hidden must be a multiple of 128 for FP8 dispatch")
+    xf = bf16_decode(x_bits).reshape(T, H // FP8_BLOCK, FP8_BLOCK)    # exact fp32
+    amax = np.max(np.abs(xf), axis=2)                                    # fp32, exact
+    nonzero = amax > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scale = np.where(nonzero, amax / FP8_MAX, np.float32(0.0)).astype(np.float32)
+        quot = (xf / scale[:, :, None]).astype(np.float32)               # fp32 division
+    quot = np.where(nonzero[:, :, None], quot, xf)                       # amax = 0: keep +-0
+    codes = e4m3_encode(quot).reshape(T, H)
+    return codes, scale
+
+
+def dispatch_fp8(x_bits, pos):
+    """FP8 dispatch: quantise each token once, write codes + scales to its rows.
+
+    Returns (codes uint8 [T*k, H], scales float32 [T*k, H/128]); rows that no
+    slot maps to hold zeros.
+    """
+    pos = np.asarray(pos)
+    T, k = pos.shape
+    codes, scale = quantize_fp8_rows(x_bits)
+    return (_scatter_rows(codes, pos, T * k, 0),
+            _scatter_rows(scale, pos, T * k, np.float32(0.0)))
+
+
+def combine(y_bits, w, pos, tokens=None, return_magnitude: bool = False):
+    """Top-k weighted gather back to token order.
+
+    out[t, h] = bf16( sum over valid j of w[t, j] * y[pos[t, j], h] ), with the
+    sum formed in fp64 and rounded to bf16 once. ``tokens`` restricts the
+    evaluation to those token indices (rows of the result follow its order).
+    With ``return_magnitude`` also returns sum_j |w[t,j] * y[pos[t,j], h]| (fp64),
+    the scale that bounds cancellation in any fp32 evaluation of the same sum.
+    """
+    y_bits = np.asarray(y_bits, dtype=np.uint16)
+    w = np.asarray(w, dtype=np.float32)
+    pos = np.asarray(pos)
+    T, k = pos.shape
+    toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    H = y_bits.shape[1]
+    acc = np.zeros((toks.shape[0], H), dtype=np.float64)
+    mag = np.zeros_like(acc)
+    for j in range(k):
+        p = pos[toks, j]
+        ok = p >= 0
+        rows = bf16_decode(y_bits[np.where(ok, p, 0)]).astype(np.float64)
+        term = w[toks, j].astype(np.float64)[:, None] * rows
+        term[~ok] = 0.0
+        acc += term
+        mag += np.abs(term)
+    out = bf16_encode(acc)
+    return (out, mag) if return_magnitude else out
+
+
+def dequant_fp8(codes, scales) -> np.ndarray:
+    """Expert-side dequantisation used by the tests: bf16(code value * scale)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.float32)
+    C, H = codes.shape
+    vals = e4m3_decode(codes).reshape(C, H // FP8_BLOCK, FP8_BLOCK)
+    prod = vals * scales.astype(np.float64)[:, :, None]                # exact in fp64
+    return bf16_encode(prod.reshape(C, H))
