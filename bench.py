@@ -1,0 +1,217 @@
+"""Benchmark: MoE dispatch & combine on one MI355X, HBM GB/s and % of peak.
+
+One step is one pass of the whole path over one batch resident in HBM:
+layout (histogram + scan + placement), bf16 dispatch, FP8 dispatch, and
+combine of the bf16-dispatched rows (identity experts), on the
+DeepSeek-V3-like shape T=4096, H=7168, E=256 in 8 virtual ranks, top-8.
+
+GB/s counts algorithmic bytes (each input read once, each output written
+once, index arrays included):
+  layout         12*S                      (S = T*k slots: ids in, pos and src_idx out)
+  dispatch bf16  2*T*H + 2*S*H + 4*S
+  dispatch FP8   2*T*H + S*H + 4*S*(H/128) + 4*S
+  combine        2*S*H + 8*S + 2*T*H
+Prints one JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+METRIC = "dispatch & combine HBM GB/s + % of peak, H=7168 T=4096 E=256 top-8"
+WORKLOAD = "deepseekv3"
+
+
+def op_bytes(T, H, k):
+    S = T * k
+    return {
+        "layout": 12 * S,
+        "dispatch_bf16": 2 * T * H + 2 * S * H + 4 * S,
+        "dispatch_fp8": 2 * T * H + S * H + 4 * S * (H // 128) + 4 * S,
+        "combine": 2 * S * H + 8 * S + 2 * T * H,
+    }
+
+
+def cpu_baseline(wl, sample_tokens: int):
+    """Time the oracle, as committed, on a sample of the same workload."""
+    import oracle
+    s = wl.shape
+    T, H, k = sample_tokens, s.hidden, s.topk
+    x = wl.x_bits[:T]
+    idx = wl.topk_idx[:T]
+    w = wl.topk_w[:T]
+    t0 = time.perf_counter()
+    lay = oracle.layout(idx, s.experts, s.ranks)
+    t1 = time.perf_counter()
+    y = oracle.dispatch_bf16(x, lay["pos"])
+    t2 = time.perf_counter()
+    oracle.dispatch_fp8(x, lay["pos"])
+    t3 = time.perf_counter()
+    oracle.combine(y, w, lay["pos"])
+    t4 = time.perf_counter()
+    b = op_bytes(T, H, k)
+    total = sum(b.values())
+    secs = t4 - t0
+    return {
+        "value": round(total / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{T} of {s.tokens} tokens of the {s.name} workload, one pass of layout, "
+                  f"bf16 dispatch, FP8 dispatch and combine (numpy, single thread); "
+                  f"{secs:.2f} s for {total} algorithmic bytes",
+        "seconds": {"layout": round(t1 - t0, 3), "dispatch_bf16": round(t2 - t1, 3),
+                    "dispatch_fp8": round(t3 - t2, 3), "combine": round(t4 - t3, 3)},
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--isolated-iters", type=int, default=30,
+                    help="per-op timings with the caches flushed before each call")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the expert-parallel work; --gpus {args.gpus} "
+              "is not supported (the inter-GPU exchange is not part of this library)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from combine_moe_dispatch_02_amd import Handle
+    from workloads import make_workload
+
+    wl = make_workload(WORKLOAD)
+    s = wl.shape
+    T, H, k, E, R = s.tokens, s.hidden, s.topk, s.experts, s.ranks
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    x = torch.from_numpy(wl.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(wl.topk_idx).to(dev)
+    w = torch.from_numpy(wl.topk_w).to(dev)
+    h = Handle(T, H, k, E, R, device=dev)
+    S = T * k
+    d_out = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+    q_out = torch.empty((S, H), dtype=torch.uint8, device=dev)
+    q_scales = torch.empty((S, H // 128), dtype=torch.float32, device=dev)
+    c_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ops = ("layout", "dispatch_bf16", "dispatch_fp8", "combine")
+
+    def run_op(name):
+        if name == "layout":
+            h.layout(idx)
+        elif name == "dispatch_bf16":
+            h.dispatch(x, out=d_out)
+        elif name == "dispatch_fp8":
+            h.dispatch(x, fp8=True, out=q_out, scales=q_scales)
+        else:
+            h.combine(d_out, w, out=c_out)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        for name in ops:
+            run_op(name)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps; per-op HIP events on the launch stream.
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)] for name in ops}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for name in ops:
+            a, b = ev[name][i]
+            a.record(stream)
+            run_op(name)
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    nbytes = op_bytes(T, H, k)
+    step_bytes = sum(nbytes.values())
+    per_op = {}
+    for name in ops:
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev[name]])
+        per_op[name] = {"bytes": nbytes[name], "us_mean": round(float(us.mean()), 2),
+                        "us_median": round(float(np.median(us)), 2),
+                        "GBps": round(nbytes[name] / (us.mean() * 1e-6) / 1e9, 1),
+                        "frac_of_peak": round(nbytes[name] / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    # Per-op timings with L2 and the 256 MB last-level cache flushed first.
+    isolated = {}
+    if args.isolated_iters > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for name in ops:
+            times = []
+            for _ in range(args.isolated_iters):
+                flush.fill_(1)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                run_op(name)
+                b.record(stream)
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b) * 1e3)
+            us = np.array(times)
+            isolated[name] = {"us_median": round(float(np.median(us)), 2),
+                              "us_p10": round(float(np.percentile(us, 10)), 2),
+                              "us_p90": round(float(np.percentile(us, 90)), 2),
+                              "GBps": round(nbytes[name] / (np.median(us) * 1e-6) / 1e9, 1)}
+        # achievable-bandwidth context: a device-to-device copy of the dispatch volume
+        src = torch.empty(nbytes["dispatch_bf16"] // 2, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        times = []
+        for _ in range(args.isolated_iters):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        isolated["copy_same_bytes"] = {"bytes": 2 * src.numel(),
+                                       "us_median": round(float(np.median(times)), 2),
+                                       "GBps": round(2 * src.numel() / (np.median(times) * 1e-6) / 1e9, 1)}
+        del flush, src, dst
+
+    dominant = max(("dispatch_bf16", "dispatch_fp8", "combine"), key=lambda n: per_op[n]["us_mean"])
+    achieved = per_op[dominant]["GBps"]
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: T={T} H={H} E={E} in R={R} virtual ranks, top-{k}; "
+                               "layout + bf16 dispatch + FP8 dispatch + bf16 combine",
+                   "tokens": T, "hidden": H, "experts": E, "virtual_ranks": R, "topk": k},
+        "frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "ops": per_op,
+        "isolated": isolated,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+"""MoE expert-parallel token dispatch and combine for one MI355X (gfx950).
+
+A thin binding over the C ABI of libmoe_ep.so (include/moe_ep.h): every step
+runs in the library's HIP kernels; this module only checks tensor
+dtypes/devices, passes raw pointers and torch's current HIP stream, and turns
+status codes into exceptions. PyTorch provides device memory and streams.
+
+Functions carry the C names (moe_dispatch_layout, moe_dispatch, moe_combine,
+...). ``Handle`` bundles them with a workspace tensor for convenience.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_EP_FP8_BLOCK, MOE_EP_MAX_EXPERTS,
+                   MOE_EP_MAX_TOPK, MOE_EP_STATUS_WORDS, MoeConfig, MoeError, MoeLayoutView)
+
+__all__ = ["Handle", "MoeError", "MoeConfig", "moe_workspace_bytes", "moe_handle_create",
+           "moe_handle_destroy", "moe_dispatch_layout", "moe_layout_view", "moe_dispatch",
+           "moe_combine", "moe_status_string", "moe_last_error", "MOE_DTYPE_BF16",
+           "MOE_DTYPE_FP8_E4M3", "MOE_EP_MAX_EXPERTS", "MOE_EP_MAX_TOPK", "MOE_EP_FP8_BLOCK"]
+
+
+def _config(max_tokens, hidden, topk, num_experts, num_ranks) -> MoeConfig:
+    return MoeConfig(int(max_tokens), int(hidden), int(topk), int(num_experts), int(num_ranks))
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None, dtype, name: str, device=None) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the handle's workspace on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def moe_workspace_bytes(max_tokens, hidden, topk, num_experts, num_ranks) -> int:
+    lib = _lib.load()
+    cfg = _config(max_tokens, hidden, topk, num_experts, num_ranks)
+    n = lib.moe_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise MoeError(_lib.MOE_ERR_UNSUPPORTED, lib.moe_last_error().decode())
+    return int(n)
+
+
+def moe_handle_create(max_tokens, hidden, topk, num_experts, num_ranks,
+                      workspace_ptr: int, workspace_bytes: int) -> int:
+    lib = _lib.load()
+    cfg = _config(max_tokens, hidden, topk, num_experts, num_ranks)
+    h = ctypes.c_void_p()
+    _lib.check(lib.moe_handle_create(ctypes.byref(cfg), ctypes.c_void_p(workspace_ptr),
+                                     workspace_bytes, ctypes.byref(h)))
+    return int(h.value)
+
+
+def moe_handle_destroy(h: int) -> None:
+    _lib.load().moe_handle_destroy(ctypes.c_void_p(h))
+
+
+def moe_dispatch_layout(h: int, topk_idx: torch.Tensor, stream=None) -> None:
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [num_tokens, topk]")
+    p = _ptr(topk_idx, torch.int32, "topk_idx")
+    _lib.check(_lib.load().moe_dispatch_layout(ctypes.c_void_p(h), ctypes.c_void_p(p),
+                                               topk_idx.shape[0], _stream(stream, topk_idx.device)))
+
+
+def moe_layout_view(h: int) -> MoeLayoutView:
+    v = MoeLayoutView()
+    _lib.check(_lib.load().moe_layout_view(ctypes.c_void_p(h), ctypes.byref(v)))
+    return v
+
+
+def moe_dispatch(h: int, x: torch.Tensor, dtype: int, out: torch.Tensor,
+                 scales: torch.Tensor | None = None, stream=None) -> None:
+    px = _ptr(x, torch.bfloat16, "x")
+    want = torch.bfloat16 if dtype == MOE_DTYPE_BF16 else torch.uint8
+    po = _ptr(out, want, "out")
+    ps = _ptr(scales, torch.float32, "scales") if dtype == MOE_DTYPE_FP8_E4M3 else None
+    _lib.check(_lib.load().moe_dispatch(ctypes.c_void_p(h), ctypes.c_void_p(px), int(dtype),
+                                        ctypes.c_void_p(po), ctypes.c_void_p(ps),
+                                        out.shape[0], _stream(stream, x.device)))
+
+
+def moe_combine(h: int, y: torch.Tensor, w: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    py = _ptr(y, torch.bfloat16, "y")
+    pw = _ptr(w, torch.float32, "w")
+    po = _ptr(out, torch.bfloat16, "out")
+    _lib.check(_lib.load().moe_combine(ctypes.c_void_p(h), ctypes.c_void_p(py), y.shape[0],
+                                       ctypes.c_void_p(pw), ctypes.c_void_p(po),
+                                       _stream(stream, y.device)))
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.load().moe_status_string(int(status)).decode()
+
+
+def moe_last_error() -> str:
+    return _lib.load().moe_last_error().decode()
+
+
+class Handle:
+    """A handle plus its caller-owned workspace tensor.
+
+    layout(topk_idx) -> dispatch(x[, fp8]) -> [experts] -> combine(y, w).
+    """
+
+    def __init__(self, max_tokens, hidden, topk, num_experts, num_ranks, device="cuda"):
+        self.max_tokens, self.hidden, self.topk = int(max_tokens), int(hidden), int(topk)
+        self.num_experts, self.num_ranks = int(num_experts), int(num_ranks)
+        nbytes = moe_workspace_bytes(max_tokens, hidden, topk, num_experts, num_ranks)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.device = self.workspace.device
+        self.h = moe_handle_create(max_tokens, hidden, topk, num_experts, num_ranks,
+                                   self.workspace.data_ptr(), nbytes)
+        self.num_tokens = None
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h:
+            moe_handle_destroy(h)
+            self.h = None
+
+    def layout(self, topk_idx: torch.Tensor, stream=None) -> None:
+        _ptr(topk_idx, torch.int32, "topk_idx", self.device)
+        moe_dispatch_layout(self.h, topk_idx, stream)
+        self.num_tokens = int(topk_idx.shape[0])
+
+    @property
+    def capacity(self) -> int:
+        return self.num_tokens * self.topk
+
+    def dispatch(self, x: torch.Tensor, fp8: bool = False, out=None, scales=None, stream=None):
+        """bf16 rows -> [capacity, H] bf16, or (uint8 codes, fp32 scales) with fp8."""
+        _ptr(x, torch.bfloat16, "x", self.device)
+        rows = self.capacity
+        if fp8:
+            if out is None:
+                out = torch.empty((rows, self.hidden), dtype=torch.uint8, device=self.device)
+            if scales is None:
+                scales = torch.empty((rows, self.hidden // MOE_EP_FP8_BLOCK), dtype=torch.float32,
+                                     device=self.device)
+            moe_dispatch(self.h, x, MOE_DTYPE_FP8_E4M3, out, scales, stream)
+            return out, scales
+        if out is None:
+            out = torch.empty((rows, self.hidden), dtype=torch.bfloat16, device=self.device)
+        moe_dispatch(self.h, x, MOE_DTYPE_BF16, out, None, stream)
+        return out
+
+    def combine(self, y: torch.Tensor, w: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+        _ptr(y, torch.bfloat16, "y", self.device)
+        if out is None:
+            out = torch.empty((self.num_tokens, self.hidden), dtype=torch.bfloat16,
+                              device=self.device)
+        moe_combine(self.h, y, w, out, stream)
+        return out
+
+    def view(self) -> dict:
+        """The last layout's arrays as int32 tensors (views into the workspace)."""
+        v = moe_layout_view(self.h)
+        base = self.workspace.data_ptr()
+
+        def arr(ptr, n):
+            off = ptr - base
+            return self.workspace[off:off + 4 * n].view(torch.int32)
+
+        E, R, T, cap = self.num_experts, self.num_ranks, v.num_tokens, v.capacity
+        return {"pos": arr(v.pos, cap).view(T, self.topk), "src_idx": arr(v.src_idx, cap),
+                "counts_e": arr(v.counts_e, E), "offsets_e": arr(v.offsets_e, E + 1),
+                "counts_r": arr(v.counts_r, R), "offsets_r": arr(v.offsets_r, R + 1),
+                "status": arr(v.status, MOE_EP_STATUS_WORDS)}

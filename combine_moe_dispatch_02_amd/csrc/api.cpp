@@ -1,0 +1,279 @@
+// C ABI of the dispatch/combine library: argument checks, workspace carving,
+// handle state and error reporting. Kernels live in layout.hip, dispatch.hip
+// and combine.hip.
+//
+// Conventions (declared in moe_ep.h): nothing throws across the ABI, host-side
+// argument errors enqueue nothing, device work is asynchronous on the caller's
+// stream, and an unsupported configuration is refused at handle creation with
+// a message that says what to change -- the fail-fast behaviour the "MoE /
+// Hybrid-EP Validation" page describes under "When EP crosses a node in an
+// intra-node-only build".
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <new>
+#include <string>
+
+#include "moe_internal.h"
+
+struct moe_handle {
+  moe_config_t cfg;
+  char* ws;
+  size_t ws_bytes;
+  moe::LayoutArrays arrays;
+  bool ready;
+  int32_t num_tokens;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxSlots = int64_t(1) << 30;  // rows and slots stay far from int32 overflow
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Region offsets inside the workspace; returns the total size.
+struct Carve {
+  size_t status, counts_e, offsets_e, counts_r, offsets_r, hist, pos, src_idx, total;
+};
+
+Carve carve(const moe_config_t& c) {
+  const int64_t slots = int64_t(c.max_tokens) * c.topk;
+  Carve r;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  r.status = take(sizeof(int32_t) * MOE_EP_STATUS_WORDS);
+  r.counts_e = take(sizeof(int32_t) * c.num_experts);
+  r.offsets_e = take(sizeof(int32_t) * (c.num_experts + 1));
+  r.counts_r = take(sizeof(int32_t) * c.num_ranks);
+  r.offsets_r = take(sizeof(int32_t) * (c.num_ranks + 1));
+  r.hist = take(sizeof(int32_t) * size_t(moe::layout_blocks(slots)) * c.num_experts);
+  r.pos = take(sizeof(int32_t) * size_t(slots));
+  r.src_idx = take(sizeof(int32_t) * size_t(slots));
+  r.total = off;
+  return r;
+}
+
+int check_config(const moe_config_t* c) {
+  if (c == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_config_t pointer is NULL");
+  if (c->max_tokens < 0)
+    return fail(MOE_ERR_INVALID_ARG, "max_tokens=%d must be >= 0", c->max_tokens);
+  if (c->hidden <= 0) return fail(MOE_ERR_INVALID_ARG, "hidden=%d must be > 0", c->hidden);
+  if (c->num_experts <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts=%d must be > 0", c->num_experts);
+  if (c->num_ranks <= 0) return fail(MOE_ERR_INVALID_ARG, "num_ranks=%d must be > 0", c->num_ranks);
+  if (c->topk <= 0) return fail(MOE_ERR_INVALID_ARG, "topk=%d must be > 0", c->topk);
+  if (c->hidden % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "hidden=%d is not a multiple of 8: rows move in 16-byte pieces; pad hidden to a "
+                "multiple of 8",
+                c->hidden);
+  if (c->num_experts > MOE_EP_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "num_experts=%d exceeds the supported maximum %d: split the experts over more "
+                "EP groups or rebuild with a larger MOE_EP_MAX_EXPERTS",
+                c->num_experts, MOE_EP_MAX_EXPERTS);
+  if (c->num_experts % c->num_ranks != 0)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "num_experts=%d is not a multiple of num_ranks=%d: each virtual rank holds a "
+                "contiguous, equal share of the experts; choose num_ranks dividing num_experts",
+                c->num_experts, c->num_ranks);
+  if (c->topk > c->num_experts)
+    return fail(MOE_ERR_UNSUPPORTED, "topk=%d exceeds num_experts=%d", c->topk, c->num_experts);
+  if (c->topk > MOE_EP_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "topk=%d exceeds the supported maximum %d", c->topk,
+                MOE_EP_MAX_TOPK);
+  if (int64_t(c->max_tokens) * c->topk > kMaxSlots)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "max_tokens*topk=%lld exceeds %lld rows: use several handles over token chunks",
+                (long long)(int64_t(c->max_tokens) * c->topk), (long long)kMaxSlots);
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_ready(moe_handle_t h, const char* fn) {
+  if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  if (!h->ready)
+    return fail(MOE_ERR_STATE, "%s: no layout yet; call moe_dispatch_layout first", fn);
+  return MOE_OK;
+}
+
+int hip_status(hipError_t err, const char* fn) {
+  if (err == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: HIP error %d (%s)", fn, int(err), hipGetErrorString(err));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config_t* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  ok();
+  return carve(*cfg).total;
+}
+
+int moe_handle_create(const moe_config_t* cfg, void* d_workspace, size_t ws_bytes,
+                      moe_handle_t* out) {
+  if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_handle_create: out is NULL");
+  *out = nullptr;
+  const int st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const Carve c = carve(*cfg);
+  if (d_workspace == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_handle_create: workspace is NULL");
+  if (!aligned(d_workspace, kAlign))
+    return fail(MOE_ERR_INVALID_ARG, "moe_handle_create: workspace must be %zu-byte aligned", kAlign);
+  if (ws_bytes < c.total)
+    return fail(MOE_ERR_INVALID_ARG, "moe_handle_create: workspace has %zu bytes, needs %zu",
+                ws_bytes, c.total);
+  moe_handle* h = new (std::nothrow) moe_handle;
+  if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_handle_create: out of host memory");
+  h->cfg = *cfg;
+  h->ws = static_cast<char*>(d_workspace);
+  h->ws_bytes = ws_bytes;
+  auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(h->ws + off); };
+  h->arrays.status = at(c.status);
+  h->arrays.counts_e = at(c.counts_e);
+  h->arrays.offsets_e = at(c.offsets_e);
+  h->arrays.counts_r = at(c.counts_r);
+  h->arrays.offsets_r = at(c.offsets_r);
+  h->arrays.hist = at(c.hist);
+  h->arrays.pos = at(c.pos);
+  h->arrays.src_idx = at(c.src_idx);
+  h->ready = false;
+  h->num_tokens = 0;
+  *out = h;
+  return ok();
+}
+
+void moe_handle_destroy(moe_handle_t h) { delete h; }
+
+int moe_dispatch_layout(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_tokens,
+                        hipStream_t stream) {
+  if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_dispatch_layout: handle is NULL");
+  if (num_tokens < 0 || num_tokens > h->cfg.max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch_layout: num_tokens=%d outside [0, %d]",
+                num_tokens, h->cfg.max_tokens);
+  if (num_tokens > 0 && d_topk_idx == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch_layout: topk_idx is NULL");
+  if (!aligned(d_topk_idx, 4))
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch_layout: topk_idx must be 4-byte aligned");
+  const hipError_t err = moe::launch_layout(d_topk_idx, num_tokens, h->cfg.topk,
+                                            h->cfg.num_experts, h->cfg.num_ranks, h->arrays, stream);
+  if (err != hipSuccess) {
+    h->ready = false;
+    return hip_status(err, "moe_dispatch_layout");
+  }
+  h->ready = true;
+  h->num_tokens = num_tokens;
+  return ok();
+}
+
+int moe_layout_view(moe_handle_t h, moe_layout_view_t* out) {
+  if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_layout_view: out is NULL");
+  const int st = check_ready(h, "moe_layout_view");
+  if (st != MOE_OK) return st;
+  out->pos = h->arrays.pos;
+  out->src_idx = h->arrays.src_idx;
+  out->counts_e = h->arrays.counts_e;
+  out->offsets_e = h->arrays.offsets_e;
+  out->counts_r = h->arrays.counts_r;
+  out->offsets_r = h->arrays.offsets_r;
+  out->status = h->arrays.status;
+  out->num_tokens = h->num_tokens;
+  out->capacity = int64_t(h->num_tokens) * h->cfg.topk;
+  return ok();
+}
+
+int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, float* d_scales,
+                 int64_t out_rows, hipStream_t stream) {
+  const int st = check_ready(h, "moe_dispatch");
+  if (st != MOE_OK) return st;
+  const int64_t capacity = int64_t(h->num_tokens) * h->cfg.topk;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: unknown dtype %d", dtype);
+  if (out_rows < capacity)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_dispatch: out_rows=%lld is below the worst-case capacity num_tokens*topk=%lld",
+                (long long)out_rows, (long long)capacity);
+  if (dtype == MOE_DTYPE_FP8_E4M3 && h->cfg.hidden % MOE_EP_FP8_BLOCK != 0)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_dispatch: FP8 needs hidden to be a multiple of %d (one scale per %d "
+                "channels); hidden=%d",
+                MOE_EP_FP8_BLOCK, MOE_EP_FP8_BLOCK, h->cfg.hidden);
+  if (h->num_tokens == 0) return ok();
+  if (d_x == nullptr || d_out == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: x or out is NULL");
+  if (!aligned(d_x, 16) || !aligned(d_out, 16))
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: x and out must be 16-byte aligned");
+  hipError_t err;
+  if (dtype == MOE_DTYPE_BF16) {
+    err = moe::launch_dispatch_bf16(d_x, h->arrays.pos, d_out, out_rows, h->num_tokens,
+                                    h->cfg.topk, h->cfg.hidden, stream);
+  } else {
+    if (d_scales == nullptr)
+      return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: FP8 dispatch needs a scales buffer");
+    if (!aligned(d_scales, 4))
+      return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: scales must be 4-byte aligned");
+    err = moe::launch_dispatch_fp8(d_x, h->arrays.pos, d_out, d_scales, out_rows,
+                                   h->num_tokens, h->cfg.topk, h->cfg.hidden, stream);
+  }
+  return hip_status(err, "moe_dispatch");
+}
+
+int moe_combine(moe_handle_t h, const void* d_y, int64_t y_rows, const float* d_w, void* d_out,
+                hipStream_t stream) {
+  const int st = check_ready(h, "moe_combine");
+  if (st != MOE_OK) return st;
+  const int64_t capacity = int64_t(h->num_tokens) * h->cfg.topk;
+  if (y_rows < capacity)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_combine: y_rows=%lld is below the capacity num_tokens*topk=%lld",
+                (long long)y_rows, (long long)capacity);
+  if (h->num_tokens == 0) return ok();
+  if (d_y == nullptr || d_w == nullptr || d_out == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: y, w or out is NULL");
+  if (!aligned(d_y, 16) || !aligned(d_out, 16) || !aligned(d_w, 4))
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_combine: y and out must be 16-byte aligned, w 4-byte aligned");
+  const hipError_t err = moe::launch_combine(d_y, y_rows, d_w, h->arrays.pos, d_out,
+                                             h->num_tokens, h->cfg.topk, h->cfg.hidden, stream);
+  return hip_status(err, "moe_combine");
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_STATE: return "MOE_ERR_STATE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal declarations shared by the library's HIP sources (not installed).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "moe_ep.h"
+
+namespace moe {
+
+// Layout kernels: one workgroup owns a contiguous chunk of slots.
+constexpr int kLayoutThreads = 512;                 // 8 wavefronts
+constexpr int kLayoutWaves = kLayoutThreads / 64;
+constexpr int kLayoutSteps = 4;                     // 64-slot steps per wavefront
+constexpr int kLayoutChunk = kLayoutThreads * kLayoutSteps;  // 2048 slots per workgroup
+
+inline int layout_blocks(int64_t slots) {
+  int64_t b = (slots + kLayoutChunk - 1) / kLayoutChunk;
+  return b < 1 ? 1 : (int)b;
+}
+
+// Device views of the workspace regions.
+struct LayoutArrays {
+  int32_t* status;     // [MOE_EP_STATUS_WORDS]
+  int32_t* counts_e;   // [E]
+  int32_t* offsets_e;  // [E + 1]
+  int32_t* counts_r;   // [R]
+  int32_t* offsets_r;  // [R + 1]
+  int32_t* hist;       // [layout_blocks(T_max * k)][E] per-workgroup histograms
+  int32_t* pos;        // [T_max * k]
+  int32_t* src_idx;    // [T_max * k]
+};
+
+// Host-side launchers; each returns the hipError_t of its launches.
+hipError_t launch_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,
+                         int num_ranks, const LayoutArrays& a, hipStream_t stream);
+
+// `rows` is the row count of the expert-major buffer; rows outside it are
+// never read or written, whatever pos holds.
+hipError_t launch_dispatch_bf16(const void* d_x, const int32_t* d_pos, void* d_out,
+                                int64_t rows, int num_tokens, int topk, int hidden,
+                                hipStream_t stream);
+
+hipError_t launch_dispatch_fp8(const void* d_x, const int32_t* d_pos, void* d_out,
+                               float* d_scales, int64_t rows, int num_tokens, int topk,
+                               int hidden, hipStream_t stream);
+
+hipError_t launch_combine(const void* d_y, int64_t rows, const float* d_w, const int32_t* d_pos,
+                          void* d_out, int num_tokens, int topk, int hidden, hipStream_t stream);
+
+}  // namespace moe

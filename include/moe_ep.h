@@ -1,0 +1,161 @@
+/*
+ * moe_ep.h -- MoE expert-parallel token dispatch and combine on one GPU
+ * (AMD Instinct MI355X, gfx950).
+ *
+ * What the operations are, per the source pages:
+ *   - "Inside the Nebius + PyTorch DeepSeek V3 recipe", section
+ *     "Mixture-of-experts and wide expert parallelism": each MoE layer has a
+ *     dispatch phase that sends every token to the experts its router chose,
+ *     and a combine phase that returns the expert outputs to the tokens'
+ *     original positions.
+ *   - Hybrid-EP news item, "Technical Structure": the library's two core
+ *     operators are dispatch and combine; "Availability and Integration":
+ *     buffers are preallocated for the worst case because routing is dynamic.
+ *   - "MoE / Hybrid-EP Validation", table "Communication path comparison"
+ *     and "FP8 dispatch restriction": dispatch may carry an FP8 payload; the
+ *     measured shape is hidden 7168, 4096 tokens per rank, top-8, EP = 8
+ *     ranks inside one node; "When EP crosses a node in an intra-node-only
+ *     build": an unsupported configuration is refused at start-up with a
+ *     message that names the fix.
+ *
+ * This library computes one EP rank's share of that work in local HBM: the
+ * expert-major receive buffer is laid out for R virtual ranks (experts split
+ * contiguously, E/R per rank), so rank r's rows form one contiguous slab.
+ *
+ * Layout rules (the pages give no formula; these are the plain readings):
+ *   - slots (t, j), t < num_tokens, j < topk, are sorted stably by expert id
+ *     in (t, j) order; pos[t*topk + j] is the row of slot (t, j);
+ *   - counts_e[e] = number of slots routed to expert e, offsets_e is their
+ *     exclusive prefix sum (E + 1 entries), counts_r / offsets_r the same per
+ *     virtual rank, src_idx[row] = token of that row;
+ *   - ids outside [0, E) are skipped: pos = -1, not counted, no row written,
+ *     no contribution to combine; status[0] counts them;
+ *   - capacity = num_tokens * topk rows (the worst case); rows at or past
+ *     offsets_e[E] are unused and have src_idx = -1.
+ *
+ * Data formats: token ids int32; activations bf16 (bit patterns, row-major
+ * [rows, hidden]); weights fp32 [num_tokens, topk]; FP8 payload OCP E4M3
+ * ("e4m3fn", max 448) bytes with one fp32 scale per 128 channels:
+ * scale = amax / 448 (fp32, correctly rounded), code = E4M3
+ * round-to-nearest-even of the fp32 quotient x / scale; an all-zero block has
+ * scale 0 and signed-zero codes. Combine: out[t] = bf16_rne(sum over j in
+ * order 0..topk-1 of w[t,j] * y[pos[t,j]]) accumulated in fp32.
+ *
+ * Conventions:
+ *   - every call returns a moe_status_t; nothing throws or aborts;
+ *   - argument errors are found on the host and then nothing is enqueued;
+ *   - device work is enqueued on the given stream and never synchronised;
+ *   - device pointers must be 16-byte aligned, rows contiguous;
+ *   - a handle is used by one stream at a time (calls on one handle from
+ *     two streams race on its workspace);
+ *   - moe_last_error() returns this thread's text for the last failure.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Limits checked at handle creation (MOE_ERR_UNSUPPORTED beyond them). */
+#define MOE_EP_MAX_EXPERTS 1024
+#define MOE_EP_MAX_TOPK 32
+#define MOE_EP_FP8_BLOCK 128
+#define MOE_EP_STATUS_WORDS 4
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, misaligned pointer, size out of range */
+  MOE_ERR_UNSUPPORTED = 2, /* configuration outside the library's limits */
+  MOE_ERR_STATE = 3,       /* dispatch/combine before a layout */
+  MOE_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} moe_status_t;
+
+typedef enum {
+  MOE_DTYPE_BF16 = 0,    /* payload rows are bf16, copied bit for bit */
+  MOE_DTYPE_FP8_E4M3 = 1 /* payload rows are E4M3 bytes + fp32 scales */
+} moe_dtype_t;
+
+/* Fixed at handle creation. max_tokens bounds num_tokens of every layout. */
+typedef struct {
+  int32_t max_tokens;  /* T_max >= 0 */
+  int32_t hidden;      /* H, multiple of 8 (of 128 for FP8 dispatch) */
+  int32_t topk;        /* k, 1 <= k <= min(E, MOE_EP_MAX_TOPK) */
+  int32_t num_experts; /* E, 1 <= E <= MOE_EP_MAX_EXPERTS */
+  int32_t num_ranks;   /* R, virtual EP ranks, E % R == 0 */
+} moe_config_t;
+
+typedef struct moe_handle* moe_handle_t;
+
+/* Device pointers into the handle's workspace, valid after a layout call has
+ * been enqueued (their contents are valid once that stream work completes). */
+typedef struct {
+  int32_t* pos;       /* [num_tokens * topk] row of each slot, -1 if skipped */
+  int32_t* src_idx;   /* [capacity] token of each row, -1 if unused */
+  int32_t* counts_e;  /* [E] */
+  int32_t* offsets_e; /* [E + 1] */
+  int32_t* counts_r;  /* [R] */
+  int32_t* offsets_r; /* [R + 1] */
+  int32_t* status;    /* [MOE_EP_STATUS_WORDS]; [0] = skipped (invalid) slots */
+  int32_t num_tokens; /* T of the last layout */
+  int64_t capacity;   /* num_tokens * topk */
+} moe_layout_view_t;
+
+/* Bytes of device workspace a handle with this configuration needs, or 0 if
+ * the configuration is invalid (moe_last_error() says why). */
+size_t moe_workspace_bytes(const moe_config_t* cfg);
+
+/* Validate cfg and bind a caller-owned device workspace (ws_bytes >=
+ * moe_workspace_bytes(cfg), 256-byte aligned). The workspace stays owned by
+ * the caller and must outlive the handle; the handle itself (host memory) is
+ * owned by the library and released by moe_handle_destroy. Enqueues nothing.
+ * MOE_ERR_UNSUPPORTED names the limit and the fix. */
+int moe_handle_create(const moe_config_t* cfg, void* d_workspace, size_t ws_bytes,
+                      moe_handle_t* out);
+
+/* Release the host-side handle; the workspace is not touched. NULL is a no-op. */
+void moe_handle_destroy(moe_handle_t h);
+
+/* Layout: histogram, exclusive scan and stable placement of the routed slots.
+ * d_topk_idx: int32 [num_tokens, topk] row-major, 0 <= num_tokens <= max_tokens.
+ * Writes pos, src_idx, counts, offsets and status into the workspace on
+ * `stream`; no host synchronisation. Marks the handle ready for dispatch and
+ * combine with this num_tokens. */
+int moe_dispatch_layout(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_tokens,
+                        hipStream_t stream);
+
+/* Device pointers and sizes of the last layout (MOE_ERR_STATE before one). */
+int moe_layout_view(moe_handle_t h, moe_layout_view_t* out);
+
+/* Dispatch: scatter token rows into the expert-major buffer.
+ * d_x: bf16 [num_tokens, hidden]. out_rows >= capacity of the last layout.
+ *   MOE_DTYPE_BF16:     d_out bf16 [out_rows, hidden], d_scales ignored;
+ *   MOE_DTYPE_FP8_E4M3: d_out uint8 [out_rows, hidden], d_scales fp32
+ *                       [out_rows, hidden / 128] (hidden % 128 == 0).
+ * Row pos[t*k+j] receives token t; rows past the valid total are not written. */
+int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, float* d_scales,
+                 int64_t out_rows, hipStream_t stream);
+
+/* Combine: top-k weighted gather back to token order.
+ * d_y: bf16 [y_rows, hidden] indexed by the same rows as dispatch,
+ * y_rows >= capacity; d_w: fp32 [num_tokens, topk]; d_out: bf16
+ * [num_tokens, hidden]. A token whose slots are all skipped gets zeros. */
+int moe_combine(moe_handle_t h, const void* d_y, int64_t y_rows, const float* d_w, void* d_out,
+                hipStream_t stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+/* This thread's message for the last failed call ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

@@ -1,0 +1,332 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Bar: layout arrays, dispatched bf16 rows, FP8 codes and fp32 scales are
+bit-exact; combine is within 1e-2 relative error (plus the fp32 cancellation
+term derived in conftest.combine_tolerance). Workloads are the five seeded
+shapes at full size, plus edge cases (empty, one token, k=1, one expert per
+rank, every slot on one expert, invalid ids, the maximum E and k, 65536
+tokens, ragged chunk tails) and an FP8 sweep that covers every bf16
+significand against every amax significand over the whole quotient range.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moe_dispatch_02_amd import Handle, MoeError
+from workloads import CONFIGS, make_expert_outputs, make_workload
+from gpu_util import (assert_combine_close, assert_layout_equal, dev_bf16, dev_f32, dev_i32,
+                      host_bits, layout_on_gpu)
+
+pytestmark = pytest.mark.gpu
+
+NAMES = [c.name for c in CONFIGS]
+
+
+def handle(shape, tokens=None, hidden=None):
+    return Handle(shape.tokens if tokens is None else tokens,
+                  shape.hidden if hidden is None else hidden,
+                  shape.topk, shape.experts, shape.ranks)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_present():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    print(f"\n[gpu] {torch.cuda.get_device_name(0)}", flush=True)
+
+
+# ---------------------------------------------------------------- layout
+
+@pytest.mark.parametrize("name", NAMES)
+def test_layout_matches_oracle(name):
+    wl = make_workload(name)
+    s = wl.shape
+    got = layout_on_gpu(handle(s), wl.topk_idx)
+    ref = oracle.layout(wl.topk_idx, s.experts, s.ranks)
+    assert_layout_equal(got, ref, s.tokens, s.topk)
+
+
+EDGE = [
+    # name, T, k, E, R, id pattern
+    ("empty", 0, 4, 16, 4, "random"),
+    ("one_token", 1, 8, 256, 8, "random"),
+    ("k1", 3000, 1, 64, 8, "random"),
+    ("one_expert_per_rank", 2500, 2, 8, 8, "random"),
+    ("every_slot_one_expert", 5000, 1, 128, 8, "const"),
+    ("duplicates_one_expert", 700, 4, 16, 4, "const"),
+    ("invalid_ids", 1500, 8, 64, 8, "invalid"),
+    ("max_experts", 2000, 8, 1024, 8, "random"),
+    ("max_topk", 600, 32, 64, 8, "random"),
+    ("ragged_tail", 2049, 3, 32, 4, "random"),
+    ("single_expert", 300, 1, 1, 1, "random"),
+    ("all_invalid", 100, 2, 8, 2, "all_invalid"),
+]
+
+
+def edge_ids(T, k, E, pattern, seed=0):
+    rng = np.random.default_rng(seed)
+    if pattern == "random":
+        return rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if pattern == "const":
+        return np.full((T, k), E - 1, dtype=np.int32)
+    if pattern == "all_invalid":
+        return np.full((T, k), -1, dtype=np.int32)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    bad = rng.random((T, k)) < 0.15
+    ids[bad] = rng.choice(np.array([-1, E, E + 77, -123456, 2**31 - 1], dtype=np.int64),
+                          size=int(bad.sum())).astype(np.int32)
+    return ids
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: c[0])
+def test_edge_cases_all_ops(case):
+    name, T, k, E, R, pattern = case
+    print(f"[edge] {name} T={T} k={k} E={E} R={R}", flush=True)
+    H = 256
+    idx = edge_ids(T, k, E, pattern)
+    h = Handle(max(T, 1), H, k, E, R)
+    got = layout_on_gpu(h, idx)
+    ref = oracle.layout(idx, E, R)
+    assert_layout_equal(got, ref, T, k)
+    total = int(ref["offsets_e"][-1])
+
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((T, H), dtype=np.float32)
+    x[:, :128] *= 0.0                                   # an all-zero FP8 block per token
+    if T:
+        x[0, 5] = -0.0
+    from workloads import bf16_bits_from_f32
+    xb = bf16_bits_from_f32(x)
+    out = host_bits(h.dispatch(dev_bf16(xb)))
+    assert np.array_equal(out[:total], oracle.dispatch_bf16(xb, ref["pos"])[:total])
+
+    codes, scales = h.dispatch(dev_bf16(xb), fp8=True)
+    rc, rs = oracle.dispatch_fp8(xb, ref["pos"])
+    assert np.array_equal(host_bits(codes)[:total], rc[:total])
+    assert np.array_equal(host_bits(scales)[:total].view(np.uint32), rs[:total].view(np.uint32))
+
+    y = make_expert_outputs(T * k, H, seed=2)
+    w = rng.uniform(-1, 1, size=(T, k)).astype(np.float32)
+    comb = host_bits(h.combine(dev_bf16(y), dev_f32(w)))
+    ref_c, mag = oracle.combine(y, w, ref["pos"], return_magnitude=True)
+    assert_combine_close(comb, ref_c, mag, k)
+
+
+def test_large_token_count_layout():
+    T, k, E, R = 65536, 8, 256, 8
+    idx = edge_ids(T, k, E, "random", seed=4)
+    got = layout_on_gpu(Handle(T, 128, k, E, R), idx)
+    ref = oracle.layout(idx, E, R)
+    assert_layout_equal(got, ref, T, k)
+
+
+def test_layout_reuse_with_fewer_tokens():
+    """A handle sized for T_max serves a smaller batch after a larger one."""
+    h = Handle(4096, 256, 8, 256, 8)
+    for T, seed in ((4096, 1), (1000, 2), (17, 3)):
+        idx = edge_ids(T, 8, 256, "random", seed=seed)
+        got = layout_on_gpu(h, idx)
+        assert_layout_equal(got, oracle.layout(idx, 256, 8), T, 8)
+
+
+# ---------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("name", NAMES)
+def test_dispatch_bf16_matches_oracle(name):
+    wl = make_workload(name)
+    s = wl.shape
+    ref = oracle.layout(wl.topk_idx, s.experts, s.ranks)
+    h = handle(s)
+    h.layout(dev_i32(wl.topk_idx))
+    out = host_bits(h.dispatch(dev_bf16(wl.x_bits)))
+    want = oracle.dispatch_bf16(wl.x_bits, ref["pos"])
+    assert np.array_equal(out, want)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_dispatch_fp8_matches_oracle(name):
+    wl = make_workload(name)
+    s = wl.shape
+    ref = oracle.layout(wl.topk_idx, s.experts, s.ranks)
+    h = handle(s)
+    h.layout(dev_i32(wl.topk_idx))
+    codes, scales = h.dispatch(dev_bf16(wl.x_bits), fp8=True)
+    rc, rs = oracle.dispatch_fp8(wl.x_bits, ref["pos"])
+    assert np.array_equal(host_bits(codes), rc)
+    assert np.array_equal(host_bits(scales).view(np.uint32), rs.view(np.uint32))
+
+
+def fp8_sweep_blocks():
+    """128-channel blocks: channel 0 holds amax, the rest sweep bf16 values.
+
+    For every amax significand (128 values, exponent 0) and a few amax values
+    at other exponents (large, small, bf16 subnormal), the swept values take
+    every significand and both signs over the 22 binades below amax, which
+    covers every E4M3 code, every rounding tie and the subnormal E4M3 range.
+    """
+    amaxes = [(127 << 7) | m for m in range(128)]                    # [1, 2)
+    amaxes += [((127 + 100) << 7) | 0x35, ((127 - 60) << 7) | 0x11,
+               (1 << 7) | 0x7F, (0 << 7) | 0x45, (0xFE << 7) | 0x7F, (127 << 7) | 0x60]
+    blocks = []
+    for a in amaxes:
+        ea = a >> 7
+        cand = []
+        for e in range(max(ea - 22, 0), ea + 1):
+            m = np.arange(128, dtype=np.uint32)
+            cand.append((e << 7) | m)
+        cand = np.concatenate(cand).astype(np.uint32)
+        cand = cand[cand <= a]
+        cand = np.concatenate([cand, cand | 0x8000, [0, 0x8000]]).astype(np.uint16)
+        for i in range(0, cand.size, 127):
+            chunk = cand[i:i + 127]
+            blk = np.zeros(128, dtype=np.uint16)
+            blk[0] = a
+            blk[1:1 + chunk.size] = chunk
+            blocks.append(blk)
+    blocks.append(np.zeros(128, np.uint16))
+    blocks.append(np.full(128, 0x8000, np.uint16))
+    return np.stack(blocks)
+
+
+def test_fp8_quantiser_sweep():
+    blocks = fp8_sweep_blocks()
+    H = 7168
+    per_row = H // 128
+    T = -(-blocks.shape[0] // per_row)
+    x = np.zeros((T * per_row, 128), dtype=np.uint16)
+    x[:blocks.shape[0]] = blocks
+    x = x.reshape(T, H)
+    print(f"[fp8 sweep] {blocks.shape[0]} blocks, T={T}", flush=True)
+    E, R, k = 8, 2, 2
+    idx = edge_ids(T, k, E, "random", seed=9)
+    ref = oracle.layout(idx, E, R)
+    h = Handle(T, H, k, E, R)
+    h.layout(dev_i32(idx))
+    codes, scales = h.dispatch(dev_bf16(x), fp8=True)
+    rc, rs = oracle.dispatch_fp8(x, ref["pos"])
+    gc, gs = host_bits(codes), host_bits(scales)
+    mism = np.argwhere(gc != rc)
+    assert mism.size == 0, f"{len(mism)} code mismatches, first at {mism[:3].tolist()}"
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
+
+
+# ---------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("name", NAMES)
+def test_combine_matches_oracle(name):
+    wl = make_workload(name)
+    s = wl.shape
+    ref = oracle.layout(wl.topk_idx, s.experts, s.ranks)
+    C = s.tokens * s.topk
+    y = make_expert_outputs(C, s.hidden, seed=wl.seed + 1)
+    h = handle(s)
+    h.layout(dev_i32(wl.topk_idx))
+    got = host_bits(h.combine(dev_bf16(y), dev_f32(wl.topk_w)))
+    if s.tokens * s.hidden <= 4096 * 7168:
+        toks = np.arange(s.tokens)
+    else:   # sampled tokens for the largest shape: first, last, and 1024 at random
+        rng = np.random.default_rng(0)
+        toks = np.unique(np.concatenate([[0, s.tokens - 1], rng.choice(s.tokens, 1024, replace=False)]))
+    want, mag = oracle.combine(y, wl.topk_w, ref["pos"], tokens=toks, return_magnitude=True)
+    rel, exact = assert_combine_close(got[toks], want, mag, s.topk)
+    print(f"[combine {name}] max rel err {rel:.3e}, bitwise-equal fraction {exact:.5f}", flush=True)
+    assert rel <= 1e-2
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_identity_experts_round_trip(name):
+    """combine(dispatch(x)) with weights summing to 1 returns x bit for bit,
+    except that -0.0 comes back as +0.0 (the weighted sum starts from +0)."""
+    wl = make_workload(name)
+    s = wl.shape
+    h = handle(s)
+    h.layout(dev_i32(wl.topk_idx))
+    y = h.dispatch(dev_bf16(wl.x_bits))
+    got = host_bits(h.combine(y, dev_f32(wl.topk_w)))
+    want = np.where(wl.x_bits == 0x8000, np.uint16(0), wl.x_bits)
+    assert np.array_equal(got, want)
+
+
+def test_fp8_pipeline_round_trip():
+    """FP8 dispatch -> expert-side dequant (torch, on the GPU) -> combine."""
+    wl = make_workload("deepseekv3_fp8")
+    s = wl.shape
+    ref = oracle.layout(wl.topk_idx, s.experts, s.ranks)
+    h = handle(s)
+    h.layout(dev_i32(wl.topk_idx))
+    codes, scales = h.dispatch(dev_bf16(wl.x_bits), fp8=True)
+    deq = (codes.view(torch.float8_e4m3fn).float().view(codes.shape[0], -1, 128)
+           * scales[:, :, None]).view(codes.shape[0], -1).to(torch.bfloat16)
+    got = host_bits(h.combine(deq, dev_f32(wl.topk_w)))
+    rc, rs = oracle.dispatch_fp8(wl.x_bits, ref["pos"])
+    y_ref = oracle.dequant_fp8(rc, rs)
+    toks = np.arange(0, s.tokens, 7)
+    want, mag = oracle.combine(y_ref, wl.topk_w, ref["pos"], tokens=toks, return_magnitude=True)
+    # torch's dequant rounds the fp32 product (double rounding vs the oracle's
+    # single rounding): allow one more bf16 half-ulp of the inputs in mag
+    rel, _ = assert_combine_close(got[toks], want, mag * (1 + 2.0 ** -8), s.topk)
+    assert rel <= 1e-2
+    x = (wl.x_bits[toks].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    g = (got[toks].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    s_tok = rs[ref["pos"][toks, 0]].astype(np.float64).repeat(128, axis=1)
+    assert np.all(np.abs(g - x) <= (2.0 ** -4 + 2.0 ** -7) * np.abs(x) + 2.0 ** -9 * s_tok + 1e-6)
+
+
+# ---------------------------------------------------------------- determinism, streams, errors
+
+def test_bitwise_deterministic_reruns():
+    wl = make_workload("deepseekv3")
+    s = wl.shape
+    h = handle(s)
+    x = dev_bf16(wl.x_bits)
+    idx = dev_i32(wl.topk_idx)
+    w = dev_f32(wl.topk_w)
+    y = dev_bf16(make_expert_outputs(s.tokens * s.topk, s.hidden, seed=5))
+    first = None
+    for _ in range(3):
+        h.layout(idx)
+        v = {k: t.clone() for k, t in h.view().items()}
+        d = h.dispatch(x)
+        q, sc = h.dispatch(x, fp8=True)
+        c = h.combine(y, w)
+        torch.cuda.synchronize()
+        cur = [v["pos"], v["src_idx"], v["counts_e"], d.view(torch.int16), q, sc.view(torch.int32),
+               c.view(torch.int16)]
+        if first is None:
+            first = cur
+        else:
+            for a, b in zip(first, cur):
+                assert torch.equal(a, b)
+
+
+def test_runs_on_a_side_stream():
+    wl = make_workload("deepseek16b")
+    s = wl.shape
+    h = handle(s)
+    x, idx, w = dev_bf16(wl.x_bits), dev_i32(wl.topk_idx), dev_f32(wl.topk_w)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        h.layout(idx)
+        y = h.dispatch(x)
+        out = h.combine(y, w)
+    side.synchronize()
+    assert np.array_equal(host_bits(out), np.where(wl.x_bits == 0x8000, np.uint16(0), wl.x_bits))
+
+
+def test_host_errors_enqueue_nothing():
+    wl = make_workload("tiny")
+    s = wl.shape
+    h = handle(s)
+    h.layout(dev_i32(wl.topk_idx))
+    x = dev_bf16(wl.x_bits)
+    small = torch.empty((s.tokens * s.topk - 1, s.hidden), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(MoeError, match="capacity"):
+        h.dispatch(x, out=small)
+    h2 = Handle(64, 200, 2, 8, 2)
+    h2.layout(dev_i32(np.zeros((4, 2), np.int32)))
+    with pytest.raises(MoeError, match="multiple of 128"):
+        h2.dispatch(dev_bf16(np.zeros((4, 200), np.uint16)), fp8=True)
+    with pytest.raises(MoeError, match="capacity"):
+        h.combine(small, dev_f32(wl.topk_w))
+    torch.cuda.synchronize()

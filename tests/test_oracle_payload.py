@@ -170,9 +170,12 @@ def test_combine_hand_worked(case):
 @pytest.mark.parametrize("name,tokens", [("tiny", 128), ("deepseek16b", 128), ("deepseekv3", 32), ("qwen3_skewed", 128)])
 def test_combine_identity_experts_returns_x(name, tokens):
     wl, lay = small_workload(name, tokens)
-    y = dispatch_bf16(wl.x_bits, lay["pos"])
+    x = wl.x_bits.copy()
+    x[:, :3] = [0x8000, 0x0000, 0x0001]             # -0, +0 and the smallest subnormal
+    y = dispatch_bf16(x, lay["pos"])
     out = combine(y, wl.topk_w, lay["pos"])
-    assert np.array_equal(out, wl.x_bits)
+    # the weighted sum starts from +0, so -0 comes back as +0; all else bit for bit
+    assert np.array_equal(out, np.where(x == 0x8000, np.uint16(0), x))
 
 
 def test_combine_unpermute_onehot_and_scaling():
