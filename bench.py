@@ -38,6 +38,29 @@ def op_bytes(T, H, k):
     }
 
 
+KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_kernel", "dispatch_fp8": "dispatch_fp8_kernel",
+                "combine": "combine_kernel"}
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "traffic_deepseekv3.json")
+
+
+def measured_traffic(op: str):
+    """HBM bytes per launch of op's kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the kernel's
+    source has changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)["kernels"][KERNEL_OF_OP[op]]
+        root = os.path.dirname(os.path.abspath(__file__))
+        with open(os.path.join(root, rec["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+                return None
+        return int(rec["traffic_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, sample_tokens: int):
     """Time the oracle, as committed, on a sample of the same workload."""
     import oracle
@@ -122,17 +145,19 @@ def main():
             run_op(name)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps; per-op HIP events on the launch stream.
-    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(args.steps)] for name in ops}
+    # Timed region: exactly K steps. HIP events on the launch stream mark every
+    # op boundary (one event between consecutive ops, so op i spans events i
+    # and i+1 of its step); each event costs a few microseconds of GPU time,
+    # which the step time includes.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        for name in ops:
-            a, b = ev[name][i]
-            a.record(stream)
+        ev[i][0].record(stream)
+        for j, name in enumerate(ops):
             run_op(name)
-            b.record(stream)
+            ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -140,21 +165,23 @@ def main():
     nbytes = op_bytes(T, H, k)
     step_bytes = sum(nbytes.values())
     per_op = {}
-    for name in ops:
-        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev[name]])
+    for j, name in enumerate(ops):
+        us = np.array([ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(args.steps)])
         per_op[name] = {"bytes": nbytes[name], "us_mean": round(float(us.mean()), 2),
                         "us_median": round(float(np.median(us)), 2),
                         "GBps": round(nbytes[name] / (us.mean() * 1e-6) / 1e9, 1),
                         "frac_of_peak": round(nbytes[name] / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    # Per-op timings with L2 and the 256 MB last-level cache flushed first.
+    # Per-op timings with L2 and the 256 MB last-level cache flushed first, by
+    # reading 1 GiB (a read leaves clean lines, so no write-back lands in the
+    # timed call).
     isolated = {}
     if args.isolated_iters > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
         for name in ops:
             times = []
             for _ in range(args.isolated_iters):
-                flush.fill_(1)
+                flush.sum()
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 run_op(name)
@@ -171,7 +198,7 @@ def main():
         dst = torch.empty_like(src)
         times = []
         for _ in range(args.isolated_iters):
-            flush.fill_(1)
+            flush.sum()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             dst.copy_(src)
@@ -204,7 +231,7 @@ def main():
         "frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant)},
         "ops": per_op,
         "isolated": isolated,
     }

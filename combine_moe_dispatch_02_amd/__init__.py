@@ -129,12 +129,13 @@ class Handle:
         self.device = self.workspace.device
         self.h = moe_handle_create(max_tokens, hidden, topk, num_experts, num_ranks,
                                    self.workspace.data_ptr(), nbytes)
+        self._destroy = _lib.load().moe_handle_destroy   # kept for use at interpreter exit
         self.num_tokens = None
 
     def __del__(self):
         h = getattr(self, "h", None)
         if h:
-            moe_handle_destroy(h)
+            self._destroy(ctypes.c_void_p(h))
             self.h = None
 
     def layout(self, topk_idx: torch.Tensor, stream=None) -> None:

@@ -46,6 +46,7 @@ int ok() {
 
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxSlots = int64_t(1) << 30;  // rows and slots stay far from int32 overflow
+constexpr int64_t kMaxItems = int64_t(1) << 30;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -104,6 +105,12 @@ int check_config(const moe_config_t* c) {
   if (c->topk > MOE_EP_MAX_TOPK)
     return fail(MOE_ERR_UNSUPPORTED, "topk=%d exceeds the supported maximum %d", c->topk,
                 MOE_EP_MAX_TOPK);
+  // Payload kernels index (token, 512-channel slice) work items with int.
+  if (int64_t(c->max_tokens) * ((c->hidden / 8 + 63) / 64) > kMaxItems)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "max_tokens=%d with hidden=%d exceeds %lld work items: use several handles over "
+                "token chunks",
+                c->max_tokens, c->hidden, (long long)kMaxItems);
   if (int64_t(c->max_tokens) * c->topk > kMaxSlots)
     return fail(MOE_ERR_UNSUPPORTED,
                 "max_tokens*topk=%lld exceeds %lld rows: use several handles over token chunks",

@@ -6,21 +6,28 @@
 // and wide expert parallelism"). Here that is
 //   out[t] = bf16_rne( sum_{j = 0..k-1, pos[t,j] >= 0} w[t,j] * y[pos[t,j]] )
 // accumulated in fp32 in the fixed slot order j = 0, 1, ..., k-1 (one fused
-// multiply-add per term), so the result does not depend on scheduling.
+// multiply-add per term, starting from +0), so the result does not depend on
+// scheduling.
 //
-// A workgroup owns whole tokens. Each lane owns 16-byte pieces of the output
-// row; for every piece it issues the loads of up to 8 slots' rows before
-// accumulating any of them, so each lane keeps 8 independent 16-byte reads in
-// flight, and writes the bf16 result with one 16-byte store.
+// Work decomposition as in dispatch: every wavefront is one (token, 1 KiB
+// column slice) work item. It fetches the token's row indices and weights
+// with scalar loads, issues the 16-byte loads of up to 8 slot rows back to
+// back (8 independent reads in flight per lane), then accumulates them in
+// slot order and writes the bf16 slice with one 16-byte store per lane.
+//
+// Combine is the last reader of the expert outputs, so those rows are read
+// with non-temporal loads, and the token rows are written with non-temporal
+// stores: neither needs to stay in L2 or the last-level cache. Measured on
+// MI355X in a dispatch -> FP8 dispatch -> combine sequence, this cut the
+// sequence from about 298 us to 274 us at T=4096, H=7168, k=8: the streamed
+// reads no longer evict (and so write back) the dirty lines the dispatches
+// left in the last-level cache.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kCombineThreads = 128;
-constexpr int kSlotBatch = 8;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -47,66 +54,70 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], float w, const u32x4
   acc[7] = __builtin_fmaf(w, bf16_hi(r.w), acc[7]);
 }
 
-template <int U>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+__global__ __launch_bounds__(64 * kItemWaves) void combine_kernel(
     const u32x4* __restrict__ y, const float* __restrict__ w, const int32_t* __restrict__ pos,
-    u32x4* __restrict__ out, int num_tokens, int topk, int nvec, int64_t rows) {
-  for (int t = blockIdx.x; t < num_tokens; t += gridDim.x) {
+    u32x4* __restrict__ out, int num_tokens, int topk, int nvec, int slices, int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int nitems = num_tokens * slices;
+  for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
+       item += gridDim.x * kItemWaves) {
+    const int t = item / slices;
+    const int v = (item - t * slices) * 64 + lane;
+    const bool active = v < nvec;
+    // Every load below is unconditional so the compiler issues them back to
+    // back: lanes past the row end read its last piece, and slots that do not
+    // contribute read a valid row (padding slots past k reuse slot k-1's row,
+    // so they cost no extra HBM traffic); their data is never used.
+    const size_t vc = active ? v : nvec - 1;
     const int32_t* pt = pos + static_cast<size_t>(t) * topk;
     const float* wt = w + static_cast<size_t>(t) * topk;
-    for (int v0 = threadIdx.x; v0 < nvec; v0 += U * kCombineThreads) {
-      float acc[U][8];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
-
-      for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
-        u32x4 r[kSlotBatch][U];
-        int p[kSlotBatch];
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
+      int p[kSlotBatch];
+      float wj[kSlotBatch];
+      bool use[kSlotBatch];
+      if (j0 + kSlotBatch <= topk) {   // full batch: contiguous, merges into wide scalar loads
 #pragma unroll
         for (int jj = 0; jj < kSlotBatch; ++jj) {
-          p[jj] = j0 + jj < topk ? pt[j0 + jj] : -1;
-          if (p[jj] >= rows) p[jj] = -1;
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int v = v0 + u * kCombineThreads;
-            r[jj][u] = u32x4{0u, 0u, 0u, 0u};
-            if (p[jj] >= 0 && v < nvec) r[jj][u] = y[static_cast<size_t>(p[jj]) * nvec + v];
-          }
+          p[jj] = pt[j0 + jj];
+          wj[jj] = wt[j0 + jj];
         }
+      } else {
 #pragma unroll
         for (int jj = 0; jj < kSlotBatch; ++jj) {
-          if (p[jj] < 0) continue;
-          const float wj = wt[j0 + jj];
-#pragma unroll
-          for (int u = 0; u < U; ++u) accumulate(acc[u], wj, r[jj][u]);
+          const int j = j0 + jj < topk ? j0 + jj : topk - 1;
+          p[jj] = pt[j];
+          wj[jj] = wt[j];
         }
       }
-
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * kCombineThreads;
-        if (v < nvec) {
-          u32x4 o;
-          o.x = pack_bf16(acc[u][0], acc[u][1]);
-          o.y = pack_bf16(acc[u][2], acc[u][3]);
-          o.z = pack_bf16(acc[u][4], acc[u][5]);
-          o.w = pack_bf16(acc[u][6], acc[u][7]);
-          out[static_cast<size_t>(t) * nvec + v] = o;
-        }
+      for (int jj = 0; jj < kSlotBatch; ++jj) {
+        const bool row_ok = p[jj] >= 0 && p[jj] < rows;
+        use[jj] = j0 + jj < topk && row_ok;
+        p[jj] = row_ok ? p[jj] : 0;
+      }
+      u32x4 r[kSlotBatch];
+#pragma unroll
+      for (int jj = 0; jj < kSlotBatch; ++jj)
+        r[jj] = __builtin_nontemporal_load(&y[static_cast<size_t>(p[jj]) * nvec + vc]);
+      // Unused slots add w * y with both zeroed: fma(0, 0, acc) == acc exactly
+      // (acc is never -0: it starts at +0 and an exact-zero sum rounds to +0).
+      // Selecting instead of branching keeps the loads above in one batch.
+#pragma unroll
+      for (int jj = 0; jj < kSlotBatch; ++jj) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        accumulate(acc, use[jj] ? wj[jj] : 0.0f, use[jj] ? r[jj] : z);
       }
     }
+    if (active) {
+      u32x4 o;
+      o.x = pack_bf16(acc[0], acc[1]);
+      o.y = pack_bf16(acc[2], acc[3]);
+      o.z = pack_bf16(acc[4], acc[5]);
+      o.w = pack_bf16(acc[6], acc[7]);
+      __builtin_nontemporal_store(o, &out[static_cast<size_t>(t) * nvec + v]);
+    }
   }
-}
-
-template <int U>
-hipError_t launch(const void* d_y, int64_t rows, const float* d_w, const int32_t* d_pos,
-                  void* d_out, int num_tokens, int topk, int nvec, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel<U>, dim3(num_tokens), dim3(kCombineThreads), 0, stream,
-                     static_cast<const u32x4*>(d_y), d_w, d_pos, static_cast<u32x4*>(d_out),
-                     num_tokens, topk, nvec, rows);
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -115,10 +126,11 @@ hipError_t launch_combine(const void* d_y, int64_t rows, const float* d_w, const
                           void* d_out, int num_tokens, int topk, int hidden, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int nvec = hidden / 8;
-  // Two 16-byte pieces per lane per pass keeps 2 x 8 row reads in flight
-  // without spilling the accumulators.
-  if (nvec <= kCombineThreads) return launch<1>(d_y, rows, d_w, d_pos, d_out, num_tokens, topk, nvec, stream);
-  return launch<2>(d_y, rows, d_w, d_pos, d_out, num_tokens, topk, nvec, stream);
+  const int slices = (nvec + 63) / 64;
+  hipLaunchKernelGGL(combine_kernel, item_grid(int64_t(num_tokens) * slices),
+                     dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_y), d_w, d_pos,
+                     static_cast<u32x4*>(d_out), num_tokens, topk, nvec, slices, rows);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -21,6 +21,11 @@ inline int layout_blocks(int64_t slots) {
   return b < 1 ? 1 : (int)b;
 }
 
+// Payload kernels: every wavefront is one independent work item, a
+// (token, column slice) pair; a workgroup is kItemWaves such items.
+constexpr int kItemWaves = 4;
+constexpr int kSlotBatch = 8;   // row indices fetched (and rows read) per batch
+
 // Device views of the workspace regions.
 struct LayoutArrays {
   int32_t* status;     // [MOE_EP_STATUS_WORDS]
@@ -49,5 +54,16 @@ hipError_t launch_dispatch_fp8(const void* d_x, const int32_t* d_pos, void* d_ou
 
 hipError_t launch_combine(const void* d_y, int64_t rows, const float* d_w, const int32_t* d_pos,
                           void* d_out, int num_tokens, int topk, int hidden, hipStream_t stream);
+
+// Index of the calling wavefront in its workgroup, as a wavefront-uniform
+// (scalar) value, so that addresses derived from it use scalar loads.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
+// Grid for num_items wavefront work items.
+inline dim3 item_grid(int64_t num_items) {
+  return dim3(static_cast<unsigned>((num_items + kItemWaves - 1) / kItemWaves));
+}
 
 }  // namespace moe
