@@ -97,9 +97,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--isolated-iters", type=int, default=30,
-                    help="per-op timings with the caches flushed before each call")
+    ap.add_argument("--sustained-iters", type=int, default=30,
+                    help="per-op timings, each op back to back over the rotating buffer sets")
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--buffer-sets", type=int, default=3,
+                    help="input/output buffer sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -118,29 +120,39 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
-    x = torch.from_numpy(wl.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    idx = torch.from_numpy(wl.topk_idx).to(dev)
-    w = torch.from_numpy(wl.topk_w).to(dev)
-    h = Handle(T, H, k, E, R, device=dev)
+    # Consecutive steps use different buffer sets (inputs and outputs, about
+    # 0.84 GB each), so no step finds the previous step's data in the 256 MB
+    # last-level cache: every step's bytes come from and go to HBM.
     S = T * k
-    d_out = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
-    q_out = torch.empty((S, H), dtype=torch.uint8, device=dev)
-    q_scales = torch.empty((S, H // 128), dtype=torch.float32, device=dev)
-    c_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    sets = []
+    for _ in range(args.buffer_sets):
+        sets.append({
+            "x": torch.from_numpy(wl.x_bits.view(np.int16)).view(torch.bfloat16).to(dev),
+            "idx": torch.from_numpy(wl.topk_idx).to(dev),
+            "w": torch.from_numpy(wl.topk_w).to(dev),
+            "d_out": torch.empty((S, H), dtype=torch.bfloat16, device=dev),
+            "q_out": torch.empty((S, H), dtype=torch.uint8, device=dev),
+            "q_scales": torch.empty((S, H // 128), dtype=torch.float32, device=dev),
+            "c_out": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+        })
+    h = Handle(T, H, k, E, R, device=dev)
     ops = ("layout", "dispatch_bf16", "dispatch_fp8", "combine")
+    cur = {"i": 0}
 
     def run_op(name):
+        b = sets[cur["i"]]
         if name == "layout":
-            h.layout(idx)
+            h.layout(b["idx"])
         elif name == "dispatch_bf16":
-            h.dispatch(x, out=d_out)
+            h.dispatch(b["x"], out=b["d_out"])
         elif name == "dispatch_fp8":
-            h.dispatch(x, fp8=True, out=q_out, scales=q_scales)
+            h.dispatch(b["x"], fp8=True, out=b["q_out"], scales=b["q_scales"])
         else:
-            h.combine(d_out, w, out=c_out)
+            h.combine(b["d_out"], b["w"], out=b["c_out"])
 
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
+        cur["i"] = i % len(sets)
         for name in ops:
             run_op(name)
     torch.cuda.synchronize()
@@ -154,6 +166,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        cur["i"] = i % len(sets)
         ev[i][0].record(stream)
         for j, name in enumerate(ops):
             run_op(name)
@@ -172,43 +185,51 @@ def main():
                         "GBps": round(nbytes[name] / (us.mean() * 1e-6) / 1e9, 1),
                         "frac_of_peak": round(nbytes[name] / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    # Per-op timings with L2 and the 256 MB last-level cache flushed first, by
-    # reading 1 GiB (a read leaves clean lines, so no write-back lands in the
-    # timed call).
-    isolated = {}
-    if args.isolated_iters > 0:
-        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    # Sustained per-op timings: each op alone, back to back over the rotating
+    # buffer sets. Every call finds the previous call's dirty lines in the
+    # last-level cache and leaves as many behind, so each call pays for its
+    # own writes reaching HBM (timing one call after a cache flush would not).
+    sustained = {}
+    if args.sustained_iters > 0:
         for name in ops:
-            times = []
-            for _ in range(args.isolated_iters):
-                flush.sum()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.sustained_iters)]
+            for i in range(3 + args.sustained_iters):
+                cur["i"] = i % len(sets)
+                if i >= 3:
+                    evs[i - 3][0].record(stream)
                 run_op(name)
-                b.record(stream)
-                torch.cuda.synchronize()
-                times.append(a.elapsed_time(b) * 1e3)
-            us = np.array(times)
-            isolated[name] = {"us_median": round(float(np.median(us)), 2),
-                              "us_p10": round(float(np.percentile(us, 10)), 2),
-                              "us_p90": round(float(np.percentile(us, 90)), 2),
-                              "GBps": round(nbytes[name] / (np.median(us) * 1e-6) / 1e9, 1)}
-        # achievable-bandwidth context: a device-to-device copy of the dispatch volume
-        src = torch.empty(nbytes["dispatch_bf16"] // 2, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        times = []
-        for _ in range(args.isolated_iters):
-            flush.sum()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            dst.copy_(src)
-            b.record(stream)
+                if i >= 3:
+                    evs[i - 3][1].record(stream)
             torch.cuda.synchronize()
-            times.append(a.elapsed_time(b) * 1e3)
-        isolated["copy_same_bytes"] = {"bytes": 2 * src.numel(),
-                                       "us_median": round(float(np.median(times)), 2),
-                                       "GBps": round(2 * src.numel() / (np.median(times) * 1e-6) / 1e9, 1)}
-        del flush, src, dst
+            us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+            sustained[name] = {"us_median": round(float(np.median(us)), 2),
+                               "us_p10": round(float(np.percentile(us, 10)), 2),
+                               "us_p90": round(float(np.percentile(us, 90)), 2),
+                               "GBps": round(nbytes[name] / (np.median(us) * 1e-6) / 1e9, 1),
+                               "frac_of_peak": round(nbytes[name] / (np.median(us) * 1e-6) / 1e9
+                                                     / HBM_PEAK_GBS, 4)}
+        # Context, same method: torch's device-to-device copy of the bf16
+        # dispatch's byte count (half read, half written) and a plain write
+        # (fill) of the bf16 dispatch's output size.
+        half = nbytes["dispatch_bf16"] // 2
+        wbytes = S * H * 2
+        bufs = [torch.empty(max(wbytes, 2 * half), dtype=torch.uint8, device=dev) for _ in range(3)]
+        for label, moved, fn in (("copy_same_bytes", 2 * half, lambda b: b[half:2 * half].copy_(b[:half])),
+                                 ("write_same_bytes", wbytes, lambda b: b[:wbytes].fill_(7))):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.sustained_iters)]
+            for i in range(3 + args.sustained_iters):
+                if i >= 3:
+                    evs[i - 3][0].record(stream)
+                fn(bufs[i % 3])
+                if i >= 3:
+                    evs[i - 3][1].record(stream)
+            torch.cuda.synchronize()
+            us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+            sustained[label] = {"bytes": moved, "us_median": round(float(np.median(us)), 2),
+                                "GBps": round(moved / (np.median(us) * 1e-6) / 1e9, 1)}
+        del bufs
 
     dominant = max(("dispatch_bf16", "dispatch_fp8", "combine"), key=lambda n: per_op[n]["us_mean"])
     achieved = per_op[dominant]["GBps"]
@@ -227,13 +248,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{WORKLOAD}: T={T} H={H} E={E} in R={R} virtual ranks, top-{k}; "
                                "layout + bf16 dispatch + FP8 dispatch + bf16 combine",
-                   "tokens": T, "hidden": H, "experts": E, "virtual_ranks": R, "topk": k},
+                   "tokens": T, "hidden": H, "experts": E, "virtual_ranks": R, "topk": k,
+                   "buffer_sets": len(sets)},
         "frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant)},
         "ops": per_op,
-        "isolated": isolated,
+        "sustained": sustained,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)

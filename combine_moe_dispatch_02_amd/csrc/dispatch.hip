@@ -17,6 +17,11 @@
 // per wavefront for bf16), and writes it to the k destination rows with
 // 16-byte stores. No two wavefronts write the same bytes: no atomics.
 //
+// Stores are ordinary (cached): the expert computation that reads the
+// dispatched rows next finds the most recent ones in the last-level cache.
+// Non-temporal stores were measured as well; over a steady stream of steps
+// whose buffers never stay cache-resident, they gave the same total time.
+//
 // FP8 E4M3 (OCP, max 448) quantisation is fused and done once per token: a
 // lane holds 16 channels, 8 consecutive lanes form one 128-channel block,
 // amax is reduced across those 8 lanes, scale = amax / 448 (IEEE division),
