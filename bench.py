@@ -100,6 +100,8 @@ def main():
     ap.add_argument("--sustained-iters", type=int, default=30,
                     help="per-op timings, each op back to back over the rotating buffer sets")
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--workgroup-sweep", type=int, default=1,
+                    help="1: also report GB/s against a cap on the payload kernels' workgroups")
     ap.add_argument("--buffer-sets", type=int, default=3,
                     help="input/output buffer sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -231,6 +233,29 @@ def main():
                                 "GBps": round(moved / (np.median(us) * 1e-6) / 1e9, 1)}
         del bufs
 
+    # Bandwidth against the number of workgroups (4 wavefronts each) the payload
+    # kernels may use (moe_set_max_workgroups), sustained method, 256 CUs.
+    sweep = {}
+    if args.workgroup_sweep:
+        for cap in (16, 32, 64, 128, 256, 512, 1024, 0):
+            h.set_max_workgroups(cap)
+            row = {}
+            for name in ("dispatch_bf16", "dispatch_fp8", "combine"):
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(5)]
+                for i in range(7):
+                    cur["i"] = i % len(sets)
+                    if i >= 2:
+                        evs[i - 2][0].record(stream)
+                    run_op(name)
+                    if i >= 2:
+                        evs[i - 2][1].record(stream)
+                torch.cuda.synchronize()
+                us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+                row[name] = round(nbytes[name] / (us * 1e-6) / 1e9, 1)
+            sweep["uncapped" if cap == 0 else str(cap)] = row
+        h.set_max_workgroups(0)
+
     dominant = max(("dispatch_bf16", "dispatch_fp8", "combine"), key=lambda n: per_op[n]["us_mean"])
     achieved = per_op[dominant]["GBps"]
     result = {
@@ -256,6 +281,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant)},
         "ops": per_op,
         "sustained": sustained,
+        "workgroup_sweep_GBps": sweep,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)

@@ -20,7 +20,8 @@ from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_EP_FP8_BLOCK, MOE_EP_
 
 __all__ = ["Handle", "MoeError", "MoeConfig", "moe_workspace_bytes", "moe_handle_create",
            "moe_handle_destroy", "moe_dispatch_layout", "moe_layout_view", "moe_dispatch",
-           "moe_combine", "moe_status_string", "moe_last_error", "MOE_DTYPE_BF16",
+           "moe_combine", "moe_set_max_workgroups", "moe_status_string", "moe_last_error",
+           "MOE_DTYPE_BF16",
            "MOE_DTYPE_FP8_E4M3", "MOE_EP_MAX_EXPERTS", "MOE_EP_MAX_TOPK", "MOE_EP_FP8_BLOCK"]
 
 
@@ -107,6 +108,10 @@ def moe_combine(h: int, y: torch.Tensor, w: torch.Tensor, out: torch.Tensor, str
                                        _stream(stream, y.device)))
 
 
+def moe_set_max_workgroups(h: int, max_workgroups: int) -> None:
+    _lib.check(_lib.load().moe_set_max_workgroups(ctypes.c_void_p(h), int(max_workgroups)))
+
+
 def moe_status_string(status: int) -> str:
     return _lib.load().moe_status_string(int(status)).decode()
 
@@ -142,6 +147,10 @@ class Handle:
         _ptr(topk_idx, torch.int32, "topk_idx", self.device)
         moe_dispatch_layout(self.h, topk_idx, stream)
         self.num_tokens = int(topk_idx.shape[0])
+
+    def set_max_workgroups(self, n: int) -> None:
+        """Cap dispatch/combine at n workgroups (0: no cap)."""
+        moe_set_max_workgroups(self.h, n)
 
     @property
     def capacity(self) -> int:

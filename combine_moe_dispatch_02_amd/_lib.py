@@ -21,7 +21,7 @@ MOE_EP_STATUS_WORDS = 4
 # Every function the header declares, for the export check.
 EXPORTS = ("moe_workspace_bytes", "moe_handle_create", "moe_handle_destroy",
            "moe_dispatch_layout", "moe_layout_view", "moe_dispatch", "moe_combine",
-           "moe_status_string", "moe_last_error")
+           "moe_set_max_workgroups", "moe_status_string", "moe_last_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -72,6 +72,7 @@ def load() -> ctypes.CDLL:
         "moe_layout_view": (ctypes.c_int, [vp, ctypes.POINTER(MoeLayoutView)]),
         "moe_dispatch": (ctypes.c_int, [vp, vp, ctypes.c_int, vp, vp, i64, vp]),
         "moe_combine": (ctypes.c_int, [vp, vp, i64, vp, vp, vp]),
+        "moe_set_max_workgroups": (ctypes.c_int, [vp, i32]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
     }

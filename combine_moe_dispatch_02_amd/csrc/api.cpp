@@ -23,6 +23,7 @@ struct moe_handle {
   moe::LayoutArrays arrays;
   bool ready;
   int32_t num_tokens;
+  int32_t max_workgroups;  // 0: one workgroup per 4 work items
 };
 
 namespace {
@@ -171,6 +172,7 @@ int moe_handle_create(const moe_config_t* cfg, void* d_workspace, size_t ws_byte
   h->arrays.src_idx = at(c.src_idx);
   h->ready = false;
   h->num_tokens = 0;
+  h->max_workgroups = 0;
   *out = h;
   return ok();
 }
@@ -238,14 +240,15 @@ int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, float*
   hipError_t err;
   if (dtype == MOE_DTYPE_BF16) {
     err = moe::launch_dispatch_bf16(d_x, h->arrays.pos, d_out, out_rows, h->num_tokens,
-                                    h->cfg.topk, h->cfg.hidden, stream);
+                                    h->cfg.topk, h->cfg.hidden, h->max_workgroups, stream);
   } else {
     if (d_scales == nullptr)
       return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: FP8 dispatch needs a scales buffer");
     if (!aligned(d_scales, 4))
       return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: scales must be 4-byte aligned");
     err = moe::launch_dispatch_fp8(d_x, h->arrays.pos, d_out, d_scales, out_rows,
-                                   h->num_tokens, h->cfg.topk, h->cfg.hidden, stream);
+                                   h->num_tokens, h->cfg.topk, h->cfg.hidden, h->max_workgroups,
+                                   stream);
   }
   return hip_status(err, "moe_dispatch");
 }
@@ -266,8 +269,18 @@ int moe_combine(moe_handle_t h, const void* d_y, int64_t y_rows, const float* d_
     return fail(MOE_ERR_INVALID_ARG,
                 "moe_combine: y and out must be 16-byte aligned, w 4-byte aligned");
   const hipError_t err = moe::launch_combine(d_y, y_rows, d_w, h->arrays.pos, d_out,
-                                             h->num_tokens, h->cfg.topk, h->cfg.hidden, stream);
+                                             h->num_tokens, h->cfg.topk, h->cfg.hidden,
+                                             h->max_workgroups, stream);
   return hip_status(err, "moe_combine");
+}
+
+int moe_set_max_workgroups(moe_handle_t h, int32_t max_workgroups) {
+  if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_set_max_workgroups: handle is NULL");
+  if (max_workgroups < 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_set_max_workgroups: max_workgroups=%d must be >= 0",
+                max_workgroups);
+  h->max_workgroups = max_workgroups;
+  return ok();
 }
 
 const char* moe_status_string(int status) {

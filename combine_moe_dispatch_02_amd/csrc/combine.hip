@@ -123,11 +123,12 @@ __global__ __launch_bounds__(64 * kItemWaves) void combine_kernel(
 }  // namespace
 
 hipError_t launch_combine(const void* d_y, int64_t rows, const float* d_w, const int32_t* d_pos,
-                          void* d_out, int num_tokens, int topk, int hidden, hipStream_t stream) {
+                          void* d_out, int num_tokens, int topk, int hidden, int max_blocks,
+                          hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int nvec = hidden / 8;
   const int slices = (nvec + 63) / 64;
-  hipLaunchKernelGGL(combine_kernel, item_grid(int64_t(num_tokens) * slices),
+  hipLaunchKernelGGL(combine_kernel, item_grid(int64_t(num_tokens) * slices, max_blocks),
                      dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_y), d_w, d_pos,
                      static_cast<u32x4*>(d_out), num_tokens, topk, nvec, slices, rows);
   return hipGetLastError();

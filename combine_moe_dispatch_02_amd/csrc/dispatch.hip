@@ -147,11 +147,11 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_fp8_kernel(
 
 hipError_t launch_dispatch_bf16(const void* d_x, const int32_t* d_pos, void* d_out,
                                 int64_t rows, int num_tokens, int topk, int hidden,
-                                hipStream_t stream) {
+                                int max_blocks, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int nvec = hidden / 8;
   const int slices = (nvec + 63) / 64;
-  hipLaunchKernelGGL(dispatch_bf16_kernel, item_grid(int64_t(num_tokens) * slices),
+  hipLaunchKernelGGL(dispatch_bf16_kernel, item_grid(int64_t(num_tokens) * slices, max_blocks),
                      dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_x), d_pos,
                      static_cast<u32x4*>(d_out), num_tokens, topk, nvec, slices, rows);
   return hipGetLastError();
@@ -159,11 +159,11 @@ hipError_t launch_dispatch_bf16(const void* d_x, const int32_t* d_pos, void* d_o
 
 hipError_t launch_dispatch_fp8(const void* d_x, const int32_t* d_pos, void* d_out,
                                float* d_scales, int64_t rows, int num_tokens, int topk,
-                               int hidden, hipStream_t stream) {
+                               int hidden, int max_blocks, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int units = hidden / 16;
   const int slices = (units + 63) / 64;
-  hipLaunchKernelGGL(dispatch_fp8_kernel, item_grid(int64_t(num_tokens) * slices),
+  hipLaunchKernelGGL(dispatch_fp8_kernel, item_grid(int64_t(num_tokens) * slices, max_blocks),
                      dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_x), d_pos,
                      static_cast<u32x4*>(d_out), d_scales, num_tokens, topk, hidden, slices, rows);
   return hipGetLastError();

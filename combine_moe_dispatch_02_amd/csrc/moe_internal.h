@@ -44,16 +44,18 @@ hipError_t launch_layout(const int32_t* d_idx, int num_tokens, int topk, int num
 
 // `rows` is the row count of the expert-major buffer; rows outside it are
 // never read or written, whatever pos holds.
+// `max_blocks` > 0 caps the grid (see item_grid).
 hipError_t launch_dispatch_bf16(const void* d_x, const int32_t* d_pos, void* d_out,
                                 int64_t rows, int num_tokens, int topk, int hidden,
-                                hipStream_t stream);
+                                int max_blocks, hipStream_t stream);
 
 hipError_t launch_dispatch_fp8(const void* d_x, const int32_t* d_pos, void* d_out,
                                float* d_scales, int64_t rows, int num_tokens, int topk,
-                               int hidden, hipStream_t stream);
+                               int hidden, int max_blocks, hipStream_t stream);
 
 hipError_t launch_combine(const void* d_y, int64_t rows, const float* d_w, const int32_t* d_pos,
-                          void* d_out, int num_tokens, int topk, int hidden, hipStream_t stream);
+                          void* d_out, int num_tokens, int topk, int hidden, int max_blocks,
+                          hipStream_t stream);
 
 // Index of the calling wavefront in its workgroup, as a wavefront-uniform
 // (scalar) value, so that addresses derived from it use scalar loads.
@@ -61,9 +63,12 @@ __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 }
 
-// Grid for num_items wavefront work items.
-inline dim3 item_grid(int64_t num_items) {
-  return dim3(static_cast<unsigned>((num_items + kItemWaves - 1) / kItemWaves));
+// Grid for num_items wavefront work items: one workgroup per kItemWaves
+// items, or at most max_blocks workgroups (> 0), whose wavefronts then loop.
+inline dim3 item_grid(int64_t num_items, int max_blocks) {
+  int64_t blocks = (num_items + kItemWaves - 1) / kItemWaves;
+  if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
+  return dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks));
 }
 
 }  // namespace moe

@@ -148,6 +148,16 @@ int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, float*
 int moe_combine(moe_handle_t h, const void* d_y, int64_t y_rows, const float* d_w, void* d_out,
                 hipStream_t stream);
 
+/* Cap the number of workgroups (of 4 wavefronts each) that moe_dispatch and
+ * moe_combine launch; 0 (the default) launches one workgroup per 4 work items.
+ * With a cap, each wavefront loops over several (token, column slice) items,
+ * so the work occupies fewer compute units and leaves the rest free for
+ * kernels on other streams -- the pages' point that the exchange should fill
+ * the link with few compute units (Hybrid-EP news item, "Efficiency
+ * Numbers"). Results are bit-identical for every cap. Negative values are
+ * MOE_ERR_INVALID_ARG. Host-side only; enqueues nothing. */
+int moe_set_max_workgroups(moe_handle_t h, int32_t max_workgroups);
+
 /* Static text for a status code. */
 const char* moe_status_string(int status);
 

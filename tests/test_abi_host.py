@@ -128,6 +128,16 @@ def test_layout_argument_errors(lib):
     lib.moe_handle_destroy(h)
 
 
+def test_max_workgroups_arguments(lib):
+    h = make_handle(lib)
+    assert lib.moe_set_max_workgroups(h, 0) == _lib.MOE_OK
+    assert lib.moe_set_max_workgroups(h, 17) == _lib.MOE_OK
+    assert lib.moe_set_max_workgroups(h, -1) == _lib.MOE_ERR_INVALID_ARG
+    assert ">= 0" in lib.moe_last_error().decode()
+    assert lib.moe_set_max_workgroups(None, 4) == _lib.MOE_ERR_INVALID_ARG
+    lib.moe_handle_destroy(h)
+
+
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(2) == b"MOE_ERR_UNSUPPORTED"

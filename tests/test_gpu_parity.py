@@ -272,6 +272,26 @@ def test_fp8_pipeline_round_trip():
     assert np.all(np.abs(g - x) <= (2.0 ** -4 + 2.0 ** -7) * np.abs(x) + 2.0 ** -9 * s_tok + 1e-6)
 
 
+@pytest.mark.parametrize("cap", [1, 7, 64, 300])
+def test_workgroup_cap_gives_identical_results(cap):
+    """Capping the grid only changes how many items each wavefront loops over."""
+    wl = make_workload("deepseekv3", tokens=600)
+    s = wl.shape
+    h = handle(s)
+    x, idx, w = dev_bf16(wl.x_bits), dev_i32(wl.topk_idx), dev_f32(wl.topk_w)
+    y = dev_bf16(make_expert_outputs(s.tokens * s.topk, s.hidden, seed=7))
+    h.layout(idx)
+    ref = [h.dispatch(x).view(torch.int16), *h.dispatch(x, fp8=True), h.combine(y, w).view(torch.int16)]
+    h.set_max_workgroups(cap)
+    got = [h.dispatch(x).view(torch.int16), *h.dispatch(x, fp8=True), h.combine(y, w).view(torch.int16)]
+    h.set_max_workgroups(0)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    lay = oracle.layout(wl.topk_idx, s.experts, s.ranks)
+    assert np.array_equal(host_bits(got[0].view(torch.bfloat16)), oracle.dispatch_bf16(wl.x_bits, lay["pos"]))
+
+
 # ---------------------------------------------------------------- determinism, streams, errors
 
 def test_bitwise_deterministic_reruns():
