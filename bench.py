@@ -233,6 +233,42 @@ def main():
                                 "GBps": round(moved / (np.median(us) * 1e-6) / 1e9, 1)}
         del bufs
 
+    # Rank-deduplicated exchange (one row per (token, rank)), sustained method.
+    exchange = {}
+    if args.sustained_iters > 0:
+        h.rank_layout(sets[0]["idx"])
+        torch.cuda.synchronize()
+        rows = int(h.rank_view()["status"][0].item())
+        cap = h.rank_capacity
+        for b in sets:
+            b["r_out"] = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+            b["r_idx"] = torch.empty((cap, k), dtype=torch.int32, device=dev)
+            b["r_w"] = torch.empty((cap, k), dtype=torch.float32, device=dev)
+        xb = {"rank_layout": 4 * S + 4 * S + 4 * T * R + 4 * rows,
+              "dispatch_ranks": 2 * T * H + 2 * rows * H + 8 * rows * k + 12 * S,
+              "combine_ranks": 2 * rows * H + 2 * T * H + 4 * T * R}
+        calls = {"rank_layout": lambda b: h.rank_layout(b["idx"]),
+                 "dispatch_ranks": lambda b: h.dispatch_ranks(b["x"], b["idx"], b["w"], out=b["r_out"],
+                                                              recv_idx=b["r_idx"], recv_w=b["r_w"]),
+                 "combine_ranks": lambda b: h.combine_ranks(b["r_out"], out=b["c_out"])}
+        for name, fn in calls.items():
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.sustained_iters)]
+            for i in range(3 + args.sustained_iters):
+                if i >= 3:
+                    evs[i - 3][0].record(stream)
+                fn(sets[i % len(sets)])
+                if i >= 3:
+                    evs[i - 3][1].record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(e) * 1e3 for a, e in evs]))
+            exchange[name] = {"bytes": xb[name], "us_median": round(us, 2),
+                              "GBps": round(xb[name] / (us * 1e-6) / 1e9, 1)}
+        exchange["rows"] = rows
+        exchange["rows_without_dedup"] = S
+        for b in sets:
+            del b["r_out"], b["r_idx"], b["r_w"]
+
     # Bandwidth against the number of workgroups (4 wavefronts each) the payload
     # kernels may use (moe_set_max_workgroups), sustained method, 256 CUs.
     sweep = {}
@@ -282,6 +318,7 @@ def main():
         "ops": per_op,
         "sustained": sustained,
         "workgroup_sweep_GBps": sweep,
+        "rank_exchange": exchange,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)

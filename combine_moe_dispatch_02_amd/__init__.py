@@ -16,11 +16,13 @@ import torch
 
 from . import _lib
 from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_EP_FP8_BLOCK, MOE_EP_MAX_EXPERTS,
-                   MOE_EP_MAX_TOPK, MOE_EP_STATUS_WORDS, MoeConfig, MoeError, MoeLayoutView)
+                   MOE_EP_MAX_TOPK, MOE_EP_STATUS_WORDS, MoeConfig, MoeError, MoeLayoutView,
+                   MoeRankLayoutView)
 
 __all__ = ["Handle", "MoeError", "MoeConfig", "moe_workspace_bytes", "moe_handle_create",
            "moe_handle_destroy", "moe_dispatch_layout", "moe_layout_view", "moe_dispatch",
-           "moe_combine", "moe_set_max_workgroups", "moe_status_string", "moe_last_error",
+           "moe_combine", "moe_rank_layout", "moe_rank_layout_view", "moe_dispatch_ranks",
+           "moe_combine_ranks", "moe_set_max_workgroups", "moe_status_string", "moe_last_error",
            "MOE_DTYPE_BF16",
            "MOE_DTYPE_FP8_E4M3", "MOE_EP_MAX_EXPERTS", "MOE_EP_MAX_TOPK", "MOE_EP_FP8_BLOCK"]
 
@@ -108,6 +110,37 @@ def moe_combine(h: int, y: torch.Tensor, w: torch.Tensor, out: torch.Tensor, str
                                        _stream(stream, y.device)))
 
 
+def moe_rank_layout(h: int, topk_idx: torch.Tensor, stream=None) -> None:
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [num_tokens, topk]")
+    p = _ptr(topk_idx, torch.int32, "topk_idx")
+    _lib.check(_lib.load().moe_rank_layout(ctypes.c_void_p(h), ctypes.c_void_p(p),
+                                           topk_idx.shape[0], _stream(stream, topk_idx.device)))
+
+
+def moe_rank_layout_view(h: int) -> MoeRankLayoutView:
+    v = MoeRankLayoutView()
+    _lib.check(_lib.load().moe_rank_layout_view(ctypes.c_void_p(h), ctypes.byref(v)))
+    return v
+
+
+def moe_dispatch_ranks(h: int, x: torch.Tensor, topk_idx: torch.Tensor, w: torch.Tensor,
+                       out: torch.Tensor, recv_idx: torch.Tensor, recv_w: torch.Tensor,
+                       stream=None) -> None:
+    args = [_ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int32, "topk_idx"),
+            _ptr(w, torch.float32, "w"), _ptr(out, torch.bfloat16, "out"),
+            _ptr(recv_idx, torch.int32, "recv_idx"), _ptr(recv_w, torch.float32, "recv_w")]
+    _lib.check(_lib.load().moe_dispatch_ranks(ctypes.c_void_p(h), *[ctypes.c_void_p(a) for a in args],
+                                              out.shape[0], _stream(stream, x.device)))
+
+
+def moe_combine_ranks(h: int, y: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    py = _ptr(y, torch.bfloat16, "y")
+    po = _ptr(out, torch.bfloat16, "out")
+    _lib.check(_lib.load().moe_combine_ranks(ctypes.c_void_p(h), ctypes.c_void_p(py), y.shape[0],
+                                             ctypes.c_void_p(po), _stream(stream, y.device)))
+
+
 def moe_set_max_workgroups(h: int, max_workgroups: int) -> None:
     _lib.check(_lib.load().moe_set_max_workgroups(ctypes.c_void_p(h), int(max_workgroups)))
 
@@ -136,6 +169,7 @@ class Handle:
                                    self.workspace.data_ptr(), nbytes)
         self._destroy = _lib.load().moe_handle_destroy   # kept for use at interpreter exit
         self.num_tokens = None
+        self.rank_num_tokens = None
 
     def __del__(self):
         h = getattr(self, "h", None)
@@ -147,6 +181,50 @@ class Handle:
         _ptr(topk_idx, torch.int32, "topk_idx", self.device)
         moe_dispatch_layout(self.h, topk_idx, stream)
         self.num_tokens = int(topk_idx.shape[0])
+
+    # ---- rank-deduplicated exchange
+    def rank_layout(self, topk_idx: torch.Tensor, stream=None) -> None:
+        _ptr(topk_idx, torch.int32, "topk_idx", self.device)
+        moe_rank_layout(self.h, topk_idx, stream)
+        self.rank_num_tokens = int(topk_idx.shape[0])
+
+    @property
+    def rank_capacity(self) -> int:
+        return self.rank_num_tokens * min(self.topk, self.num_ranks)
+
+    def dispatch_ranks(self, x, topk_idx, w, out=None, recv_idx=None, recv_w=None, stream=None):
+        """One bf16 row per (token, rank) + receiver metadata (local ids, weights)."""
+        rows = self.rank_capacity
+        if out is None:
+            out = torch.empty((rows, self.hidden), dtype=torch.bfloat16, device=self.device)
+        if recv_idx is None:
+            recv_idx = torch.empty((rows, self.topk), dtype=torch.int32, device=self.device)
+        if recv_w is None:
+            recv_w = torch.empty((rows, self.topk), dtype=torch.float32, device=self.device)
+        moe_dispatch_ranks(self.h, x, topk_idx, w, out, recv_idx, recv_w, stream)
+        return out, recv_idx, recv_w
+
+    def combine_ranks(self, y, out=None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty((self.rank_num_tokens, self.hidden), dtype=torch.bfloat16,
+                              device=self.device)
+        moe_combine_ranks(self.h, y, out, stream)
+        return out
+
+    def rank_view(self) -> dict:
+        """The last rank layout's arrays as int32 tensors (views into the workspace)."""
+        v = moe_rank_layout_view(self.h)
+        base = self.workspace.data_ptr()
+
+        def arr(ptr, n):
+            off = ptr - base
+            return self.workspace[off:off + 4 * n].view(torch.int32)
+
+        R, T, cap = self.num_ranks, v.num_tokens, v.capacity
+        return {"rank_pos": arr(v.rank_pos, T * R).view(T, R),
+                "slot_row": arr(v.slot_row, T * self.topk).view(T, self.topk),
+                "rank_src": arr(v.src_idx, cap), "counts_r": arr(v.counts_r, R),
+                "offsets_r": arr(v.offsets_r, R + 1), "status": arr(v.status, MOE_EP_STATUS_WORDS)}
 
     def set_max_workgroups(self, n: int) -> None:
         """Cap dispatch/combine at n workgroups (0: no cap)."""

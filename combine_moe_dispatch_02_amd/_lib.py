@@ -21,6 +21,7 @@ MOE_EP_STATUS_WORDS = 4
 # Every function the header declares, for the export check.
 EXPORTS = ("moe_workspace_bytes", "moe_handle_create", "moe_handle_destroy",
            "moe_dispatch_layout", "moe_layout_view", "moe_dispatch", "moe_combine",
+           "moe_rank_layout", "moe_rank_layout_view", "moe_dispatch_ranks", "moe_combine_ranks",
            "moe_set_max_workgroups", "moe_status_string", "moe_last_error")
 
 
@@ -36,6 +37,13 @@ class MoeLayoutView(ctypes.Structure):
                 ("counts_r", ctypes.c_void_p), ("offsets_r", ctypes.c_void_p),
                 ("status", ctypes.c_void_p), ("num_tokens", ctypes.c_int32),
                 ("capacity", ctypes.c_int64)]
+
+
+class MoeRankLayoutView(ctypes.Structure):
+    _fields_ = [("rank_pos", ctypes.c_void_p), ("slot_row", ctypes.c_void_p),
+                ("src_idx", ctypes.c_void_p), ("counts_r", ctypes.c_void_p),
+                ("offsets_r", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("num_tokens", ctypes.c_int32), ("capacity", ctypes.c_int64)]
 
 
 class MoeError(RuntimeError):
@@ -72,6 +80,10 @@ def load() -> ctypes.CDLL:
         "moe_layout_view": (ctypes.c_int, [vp, ctypes.POINTER(MoeLayoutView)]),
         "moe_dispatch": (ctypes.c_int, [vp, vp, ctypes.c_int, vp, vp, i64, vp]),
         "moe_combine": (ctypes.c_int, [vp, vp, i64, vp, vp, vp]),
+        "moe_rank_layout": (ctypes.c_int, [vp, vp, i32, vp]),
+        "moe_rank_layout_view": (ctypes.c_int, [vp, ctypes.POINTER(MoeRankLayoutView)]),
+        "moe_dispatch_ranks": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+        "moe_combine_ranks": (ctypes.c_int, [vp, vp, i64, vp, vp]),
         "moe_set_max_workgroups": (ctypes.c_int, [vp, i32]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),

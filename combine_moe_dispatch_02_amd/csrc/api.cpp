@@ -21,8 +21,11 @@ struct moe_handle {
   char* ws;
   size_t ws_bytes;
   moe::LayoutArrays arrays;
+  moe::RankArrays rank;
   bool ready;
   int32_t num_tokens;
+  bool rank_ready;
+  int32_t rank_num_tokens;
   int32_t max_workgroups;  // 0: one workgroup per 4 work items
 };
 
@@ -53,7 +56,9 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Region offsets inside the workspace; returns the total size.
 struct Carve {
-  size_t status, counts_e, offsets_e, counts_r, offsets_r, hist, pos, src_idx, total;
+  size_t status, counts_e, offsets_e, counts_r, offsets_r, hist, pos, src_idx;
+  size_t r_status, r_counts, r_offsets, r_hist, r_slot_row, r_rank_pos, r_src;
+  size_t total;
 };
 
 Carve carve(const moe_config_t& c) {
@@ -73,6 +78,14 @@ Carve carve(const moe_config_t& c) {
   r.hist = take(sizeof(int32_t) * size_t(moe::layout_blocks(slots)) * c.num_experts);
   r.pos = take(sizeof(int32_t) * size_t(slots));
   r.src_idx = take(sizeof(int32_t) * size_t(slots));
+  const int64_t rank_rows = int64_t(c.max_tokens) * (c.topk < c.num_ranks ? c.topk : c.num_ranks);
+  r.r_status = take(sizeof(int32_t) * MOE_EP_STATUS_WORDS);
+  r.r_counts = take(sizeof(int32_t) * c.num_ranks);
+  r.r_offsets = take(sizeof(int32_t) * (c.num_ranks + 1));
+  r.r_hist = take(sizeof(int32_t) * size_t(moe::layout_blocks(slots)) * c.num_ranks);
+  r.r_slot_row = take(sizeof(int32_t) * size_t(slots));
+  r.r_rank_pos = take(sizeof(int32_t) * size_t(c.max_tokens) * c.num_ranks);
+  r.r_src = take(sizeof(int32_t) * size_t(rank_rows));
   r.total = off;
   return r;
 }
@@ -128,6 +141,18 @@ int check_ready(moe_handle_t h, const char* fn) {
   return MOE_OK;
 }
 
+int64_t rank_capacity(const moe_handle* h) {
+  return int64_t(h->rank_num_tokens) * (h->cfg.topk < h->cfg.num_ranks ? h->cfg.topk
+                                                                         : h->cfg.num_ranks);
+}
+
+int check_rank_ready(moe_handle_t h, const char* fn) {
+  if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  if (!h->rank_ready)
+    return fail(MOE_ERR_STATE, "%s: no rank layout yet; call moe_rank_layout first", fn);
+  return MOE_OK;
+}
+
 int hip_status(hipError_t err, const char* fn) {
   if (err == hipSuccess) return ok();
   return fail(MOE_ERR_HIP, "%s: HIP error %d (%s)", fn, int(err), hipGetErrorString(err));
@@ -170,8 +195,17 @@ int moe_handle_create(const moe_config_t* cfg, void* d_workspace, size_t ws_byte
   h->arrays.hist = at(c.hist);
   h->arrays.pos = at(c.pos);
   h->arrays.src_idx = at(c.src_idx);
+  h->rank.status = at(c.r_status);
+  h->rank.counts = at(c.r_counts);
+  h->rank.offsets = at(c.r_offsets);
+  h->rank.hist = at(c.r_hist);
+  h->rank.slot_row = at(c.r_slot_row);
+  h->rank.rank_pos = at(c.r_rank_pos);
+  h->rank.src = at(c.r_src);
   h->ready = false;
   h->num_tokens = 0;
+  h->rank_ready = false;
+  h->rank_num_tokens = 0;
   h->max_workgroups = 0;
   *out = h;
   return ok();
@@ -272,6 +306,91 @@ int moe_combine(moe_handle_t h, const void* d_y, int64_t y_rows, const float* d_
                                              h->num_tokens, h->cfg.topk, h->cfg.hidden,
                                              h->max_workgroups, stream);
   return hip_status(err, "moe_combine");
+}
+
+int moe_rank_layout(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_tokens,
+                    hipStream_t stream) {
+  if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_rank_layout: handle is NULL");
+  if (num_tokens < 0 || num_tokens > h->cfg.max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "moe_rank_layout: num_tokens=%d outside [0, %d]", num_tokens,
+                h->cfg.max_tokens);
+  if (num_tokens > 0 && d_topk_idx == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_rank_layout: topk_idx is NULL");
+  if (!aligned(d_topk_idx, 4))
+    return fail(MOE_ERR_INVALID_ARG, "moe_rank_layout: topk_idx must be 4-byte aligned");
+  const hipError_t err = moe::launch_rank_layout(d_topk_idx, num_tokens, h->cfg.topk,
+                                                 h->cfg.num_experts, h->cfg.num_ranks, h->rank,
+                                                 stream);
+  if (err != hipSuccess) {
+    h->rank_ready = false;
+    return hip_status(err, "moe_rank_layout");
+  }
+  h->rank_ready = true;
+  h->rank_num_tokens = num_tokens;
+  return ok();
+}
+
+int moe_rank_layout_view(moe_handle_t h, moe_rank_layout_view_t* out) {
+  if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_rank_layout_view: out is NULL");
+  const int st = check_rank_ready(h, "moe_rank_layout_view");
+  if (st != MOE_OK) return st;
+  out->rank_pos = h->rank.rank_pos;
+  out->slot_row = h->rank.slot_row;
+  out->src_idx = h->rank.src;
+  out->counts_r = h->rank.counts;
+  out->offsets_r = h->rank.offsets;
+  out->status = h->rank.status;
+  out->num_tokens = h->rank_num_tokens;
+  out->capacity = rank_capacity(h);
+  return ok();
+}
+
+int moe_dispatch_ranks(moe_handle_t h, const void* d_x, const int32_t* d_topk_idx,
+                       const float* d_w, void* d_out, int32_t* d_recv_idx, float* d_recv_w,
+                       int64_t out_rows, hipStream_t stream) {
+  const int st = check_rank_ready(h, "moe_dispatch_ranks");
+  if (st != MOE_OK) return st;
+  const int64_t capacity = rank_capacity(h);
+  if (out_rows < capacity)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_dispatch_ranks: out_rows=%lld is below the capacity num_tokens*min(topk,R)=%lld",
+                (long long)out_rows, (long long)capacity);
+  if (h->rank_num_tokens == 0) return ok();
+  if (d_x == nullptr || d_topk_idx == nullptr || d_w == nullptr || d_out == nullptr ||
+      d_recv_idx == nullptr || d_recv_w == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch_ranks: a pointer argument is NULL");
+  if (!aligned(d_x, 16) || !aligned(d_out, 16) || !aligned(d_topk_idx, 4) || !aligned(d_w, 4) ||
+      !aligned(d_recv_idx, 4) || !aligned(d_recv_w, 4))
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_dispatch_ranks: x and out must be 16-byte aligned, the rest 4-byte aligned");
+  hipError_t err = moe::launch_dispatch_bf16(d_x, h->rank.slot_row, d_out, out_rows,
+                                             h->rank_num_tokens, h->cfg.topk, h->cfg.hidden,
+                                             h->max_workgroups, stream);
+  if (err == hipSuccess)
+    err = moe::launch_rank_meta(d_topk_idx, d_w, h->rank.slot_row, h->rank_num_tokens,
+                                h->cfg.topk, h->cfg.num_experts, h->cfg.num_ranks, out_rows,
+                                d_recv_idx, d_recv_w, stream);
+  return hip_status(err, "moe_dispatch_ranks");
+}
+
+int moe_combine_ranks(moe_handle_t h, const void* d_y, int64_t y_rows, void* d_out,
+                      hipStream_t stream) {
+  const int st = check_rank_ready(h, "moe_combine_ranks");
+  if (st != MOE_OK) return st;
+  const int64_t capacity = rank_capacity(h);
+  if (y_rows < capacity)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_combine_ranks: y_rows=%lld is below the capacity num_tokens*min(topk,R)=%lld",
+                (long long)y_rows, (long long)capacity);
+  if (h->rank_num_tokens == 0) return ok();
+  if (d_y == nullptr || d_out == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine_ranks: y or out is NULL");
+  if (!aligned(d_y, 16) || !aligned(d_out, 16))
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine_ranks: y and out must be 16-byte aligned");
+  const hipError_t err =
+      moe::launch_combine_ranks(d_y, y_rows, h->rank.rank_pos, d_out, h->rank_num_tokens,
+                                h->cfg.num_ranks, h->cfg.hidden, h->max_workgroups, stream);
+  return hip_status(err, "moe_combine_ranks");
 }
 
 int moe_set_max_workgroups(moe_handle_t h, int32_t max_workgroups) {

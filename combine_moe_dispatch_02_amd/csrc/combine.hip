@@ -54,6 +54,10 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], float w, const u32x4
   acc[7] = __builtin_fmaf(w, bf16_hi(r.w), acc[7]);
 }
 
+// kWeighted = false sums the rows unweighted (weight 1, w unused): the final
+// reduction of the rank-deduplicated exchange, over the per-rank partial rows
+// of each token in ascending rank order.
+template <bool kWeighted>
 __global__ __launch_bounds__(64 * kItemWaves) void combine_kernel(
     const u32x4* __restrict__ y, const float* __restrict__ w, const int32_t* __restrict__ pos,
     u32x4* __restrict__ out, int num_tokens, int topk, int nvec, int slices, int64_t rows) {
@@ -70,7 +74,7 @@ __global__ __launch_bounds__(64 * kItemWaves) void combine_kernel(
     // so they cost no extra HBM traffic); their data is never used.
     const size_t vc = active ? v : nvec - 1;
     const int32_t* pt = pos + static_cast<size_t>(t) * topk;
-    const float* wt = w + static_cast<size_t>(t) * topk;
+    const float* wt = kWeighted ? w + static_cast<size_t>(t) * topk : nullptr;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
       int p[kSlotBatch];
@@ -80,14 +84,14 @@ __global__ __launch_bounds__(64 * kItemWaves) void combine_kernel(
 #pragma unroll
         for (int jj = 0; jj < kSlotBatch; ++jj) {
           p[jj] = pt[j0 + jj];
-          wj[jj] = wt[j0 + jj];
+          wj[jj] = kWeighted ? wt[j0 + jj] : 1.0f;
         }
       } else {
 #pragma unroll
         for (int jj = 0; jj < kSlotBatch; ++jj) {
           const int j = j0 + jj < topk ? j0 + jj : topk - 1;
           p[jj] = pt[j];
-          wj[jj] = wt[j];
+          wj[jj] = kWeighted ? wt[j] : 1.0f;
         }
       }
 #pragma unroll
@@ -128,9 +132,22 @@ hipError_t launch_combine(const void* d_y, int64_t rows, const float* d_w, const
   if (num_tokens == 0) return hipSuccess;
   const int nvec = hidden / 8;
   const int slices = (nvec + 63) / 64;
-  hipLaunchKernelGGL(combine_kernel, item_grid(int64_t(num_tokens) * slices, max_blocks),
+  hipLaunchKernelGGL(combine_kernel<true>, item_grid(int64_t(num_tokens) * slices, max_blocks),
                      dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_y), d_w, d_pos,
                      static_cast<u32x4*>(d_out), num_tokens, topk, nvec, slices, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_ranks(const void* d_y, int64_t rows, const int32_t* d_rank_pos,
+                                void* d_out, int num_tokens, int num_ranks, int hidden,
+                                int max_blocks, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int nvec = hidden / 8;
+  const int slices = (nvec + 63) / 64;
+  hipLaunchKernelGGL(combine_kernel<false>, item_grid(int64_t(num_tokens) * slices, max_blocks),
+                     dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_y), nullptr,
+                     d_rank_pos, static_cast<u32x4*>(d_out), num_tokens, num_ranks, nvec, slices,
+                     rows);
   return hipGetLastError();
 }
 

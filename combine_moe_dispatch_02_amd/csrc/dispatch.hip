@@ -143,7 +143,43 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_fp8_kernel(
   }
 }
 
+// Receiver metadata of the rank-deduplicated exchange. One thread per slot
+// (t, j): for each (token, rank) row p of token t (opened by slot jr), entry
+// (p, j) says whether slot j's expert lives on that row's rank -- its local id
+// e - r*E/R and its weight -- or not (-1 and 0).
+__global__ __launch_bounds__(256) void rank_meta_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ w,
+    const int32_t* __restrict__ slot_row, int num_tokens, int topk, int num_experts,
+    int per_rank, int64_t rows, int32_t* __restrict__ recv_idx, float* __restrict__ recv_w) {
+  const int slot = blockIdx.x * blockDim.x + threadIdx.x;
+  if (slot >= num_tokens * topk) return;
+  const int t = slot / topk, j = slot - t * topk;
+  const int e = idx[slot];
+  const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(num_experts);
+  const int r = valid ? e / per_rank : -1;
+  const float wj = w[slot];
+  for (int jr = 0; jr < topk; ++jr) {
+    const int p = slot_row[t * topk + jr];
+    if (p < 0 || p >= rows) continue;
+    const int rr = idx[t * topk + jr] / per_rank;   // the opening slot's expert is valid
+    const bool local = valid && r == rr;
+    recv_idx[static_cast<size_t>(p) * topk + j] = local ? e - rr * per_rank : -1;
+    recv_w[static_cast<size_t>(p) * topk + j] = local ? wj : 0.0f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rank_meta(const int32_t* d_idx, const float* d_w, const int32_t* d_slot_row,
+                            int num_tokens, int topk, int num_experts, int num_ranks, int64_t rows,
+                            int32_t* d_recv_idx, float* d_recv_w, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int slots = num_tokens * topk;
+  hipLaunchKernelGGL(rank_meta_kernel, dim3((slots + 255) / 256), dim3(256), 0, stream, d_idx, d_w,
+                     d_slot_row, num_tokens, topk, num_experts, num_experts / num_ranks, rows,
+                     d_recv_idx, d_recv_w);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch_bf16(const void* d_x, const int32_t* d_pos, void* d_out,
                                 int64_t rows, int num_tokens, int topk, int hidden,

@@ -8,6 +8,10 @@
 // The placement is the stable counting sort of the T*k slots by expert id in
 // (token, slot) order, with experts split contiguously over R virtual ranks.
 //
+// The same two kernels also build the rank-deduplicated layout (one row per
+// (token, virtual rank) pair, the rows an expert-parallel exchange actually
+// sends); the pass is selected at compile time (see Buckets).
+//
 // Two launches, no grid-wide synchronisation:
 //   1. layout_hist_kernel   -- each workgroup counts the expert ids of its own
 //      chunk of 2048 slots into an LDS histogram and writes it out.
@@ -42,58 +46,135 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, bool valid, int nbi
   return valid ? peers : 0ull;
 }
 
-__global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(
-    const int32_t* __restrict__ idx, int slots, int num_experts, int nbits,
-    int32_t* __restrict__ hist) {
+// What a layout pass sorts: every slot (t, j) falls into one bucket, or none.
+//   expert pass: bucket = the slot's expert id;
+//   rank pass:   bucket = the rank holding the slot's expert, but only for the
+//                first slot of the token that reaches that rank, so that each
+//                (token, rank) pair is counted and placed exactly once.
+// Slots whose expert id lies outside [0, E) fall into no bucket.
+struct Buckets {
+  const int32_t* idx;  // [T * k] expert ids
+  int slots;           // T * k
+  int topk;            // k
+  int num_experts;     // E
+  uint32_t rank_mul;   // ceil(2^20 / (E / R)): rank = (e * rank_mul) >> 20, exact for E <= 1024
+  int nbuckets;        // E (expert pass) or R (rank pass)
+  int nbits;           // bits of a bucket id
+  int capacity;        // rows: T * k (expert pass) or T * min(k, R) (rank pass)
+};
+
+// Where a pass writes (pointers into the workspace).
+struct LayoutOut {
+  int32_t* hist;           // [workgroups][nbuckets]
+  int32_t* counts;         // [nbuckets]
+  int32_t* offsets;        // [nbuckets + 1]
+  int32_t* group_counts;   // expert pass: per-rank counts [R]
+  int32_t* group_offsets;  // expert pass: per-rank offsets [R + 1]
+  int32_t* pos;            // [T * k] row of each bucketed slot, -1 otherwise
+  int32_t* src;            // [capacity] token of each row, -1 past the total
+  int32_t* status;         // [MOE_EP_STATUS_WORDS]
+  int32_t* rank_pos;       // rank pass: [T * R] row of each (token, rank), -1 if none
+  int num_groups;          // R
+  int per_rank;            // E / R
+};
+
+__device__ __forceinline__ int rank_of(const Buckets& b, int e) {
+  return static_cast<int>((static_cast<uint32_t>(e) * b.rank_mul) >> 20);
+}
+
+// Buckets of this wavefront's kLayoutSteps 64-slot steps starting at `base`
+// (lane l of step s holds slot base + 64 s + l). Every lane must call it.
+template <bool kRanks>
+__device__ __forceinline__ void load_buckets(const Buckets& b, int base, int lane,
+                                             int (&ids)[kLayoutSteps]) {
+  int raw[kLayoutSteps];
+#pragma unroll
+  for (int s = 0; s < kLayoutSteps; ++s) {
+    const int slot = base + s * 64 + lane;
+    raw[s] = slot < b.slots ? b.idx[slot] : -1;
+  }
+#pragma unroll
+  for (int s = 0; s < kLayoutSteps; ++s) {
+    const int e = raw[s];
+    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(b.num_experts);
+    if (!kRanks) {
+      ids[s] = valid ? e : -1;
+      continue;
+    }
+    // A slot opens its (token, rank) pair unless an earlier slot of the same
+    // token reaches the same rank. The d-th earlier slot sits d lanes below in
+    // the same step, or, for a token that starts in the previous step, in
+    // memory (read only then).
+    const int slot = base + s * 64 + lane;
+    const int r = valid ? rank_of(b, e) : -1;
+    const int j = slot % b.topk;
+    bool first = valid;
+    for (int d = 1; d < b.topk; ++d) {   // uniform trip count: every lane shuffles
+      const int other = __shfl(r, lane >= d ? lane - d : lane, 64);
+      if (valid && d <= j) {   // slot - d >= t*k >= 0 and slot < slots
+        int ro = other;
+        if (lane < d) {
+          const int f = b.idx[slot - d];
+          ro = static_cast<unsigned>(f) < static_cast<unsigned>(b.num_experts) ? rank_of(b, f) : -1;
+        }
+        if (ro == r) first = false;
+      }
+    }
+    ids[s] = first ? r : -1;
+  }
+}
+
+template <bool kRanks>
+__global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(Buckets b, LayoutOut o) {
   __shared__ int32_t s_hist[MOE_EP_MAX_EXPERTS];
   const int tid = threadIdx.x;
-  for (int e = tid; e < num_experts; e += kLayoutThreads) s_hist[e] = 0;
+  for (int e = tid; e < b.nbuckets; e += kLayoutThreads) s_hist[e] = 0;
+  if (kRanks) {   // every (token, rank) starts as "not routed there"
+    const int cells = (b.slots / b.topk) * o.num_groups;
+    for (int i = blockIdx.x * kLayoutThreads + tid; i < cells; i += gridDim.x * kLayoutThreads)
+      o.rank_pos[i] = -1;
+  }
   __syncthreads();
 
   const int lane = tid & 63;
   const int base = blockIdx.x * kLayoutChunk + (tid >> 6) * (kLayoutSteps * 64);
   int ids[kLayoutSteps];
-#pragma unroll
-  for (int s = 0; s < kLayoutSteps; ++s) {
-    const int slot = base + s * 64 + lane;
-    ids[s] = slot < slots ? idx[slot] : -1;
-  }
+  load_buckets<kRanks>(b, base, lane, ids);
 #pragma unroll
   for (int s = 0; s < kLayoutSteps; ++s) {
     const int e = ids[s];
-    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(num_experts);
-    const uint64_t peers = same_expert_lanes(e, valid, nbits);
+    const bool valid = e >= 0;
+    const uint64_t peers = same_expert_lanes(e, valid, b.nbits);
     if (valid && lanes_below(peers) == 0) atomicAdd(&s_hist[e], __popcll(peers));
   }
   __syncthreads();
-  int32_t* out = hist + static_cast<size_t>(blockIdx.x) * num_experts;
-  for (int e = tid; e < num_experts; e += kLayoutThreads) out[e] = s_hist[e];
+  int32_t* out = o.hist + static_cast<size_t>(blockIdx.x) * b.nbuckets;
+  for (int e = tid; e < b.nbuckets; e += kLayoutThreads) out[e] = s_hist[e];
 }
 
-__global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(
-    const int32_t* __restrict__ idx, int slots, int topk, int num_experts, int num_ranks,
-    int nbits, const int32_t* __restrict__ hist, LayoutArrays a) {
-  // s_cur[w * E + e]: wavefront w's running row cursor for expert e.
+template <bool kRanks>
+__global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b, LayoutOut o) {
+  // s_cur[w * E + e]: wavefront w's running row cursor for bucket e.
   __shared__ int32_t s_cur[kLayoutWaves * MOE_EP_MAX_EXPERTS];
   __shared__ int32_t s_off[MOE_EP_MAX_EXPERTS + 1];
   __shared__ int32_t s_pre[MOE_EP_MAX_EXPERTS];
   __shared__ int32_t s_wsum[kLayoutWaves];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int E = num_experts;
+  const int E = b.nbuckets;
   const int nblocks = gridDim.x;
 
   for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) s_cur[i] = 0;
 
-  // Column sums of the per-workgroup histograms: the expert totals, and the
+  // Column sums of the per-workgroup histograms: the bucket totals, and the
   // part that earlier workgroups (earlier slots) contribute.
   for (int e = tid; e < E; e += kLayoutThreads) {
     int tot = 0, pre = 0;
 #pragma unroll 16
-    for (int b = 0; b < nblocks; ++b) {
-      const int v = hist[static_cast<size_t>(b) * E + e];
+    for (int g = 0; g < nblocks; ++g) {
+      const int v = o.hist[static_cast<size_t>(g) * E + e];
       tot += v;
-      pre += b < static_cast<int>(blockIdx.x) ? v : 0;
+      pre += g < static_cast<int>(blockIdx.x) ? v : 0;
     }
     s_off[e] = tot;
     s_pre[e] = pre;
@@ -104,23 +185,19 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(
   const int base = blockIdx.x * kLayoutChunk + wave * (kLayoutSteps * 64);
   int ids[kLayoutSteps];
   uint64_t peers[kLayoutSteps];
-#pragma unroll
-  for (int s = 0; s < kLayoutSteps; ++s) {
-    const int slot = base + s * 64 + lane;
-    ids[s] = slot < slots ? idx[slot] : -1;
-  }
+  load_buckets<kRanks>(b, base, lane, ids);
   int32_t* my_cur = s_cur + wave * E;
 #pragma unroll
   for (int s = 0; s < kLayoutSteps; ++s) {
     const int e = ids[s];
-    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
-    peers[s] = same_expert_lanes(e, valid, nbits);
+    const bool valid = e >= 0;
+    peers[s] = same_expert_lanes(e, valid, b.nbits);
     // Group leaders hold distinct ids within a step and the row belongs to
     // this wavefront alone, so a plain read-modify-write is race free.
     if (valid && lanes_below(peers[s]) == 0) my_cur[e] += __popcll(peers[s]);
   }
 
-  // Exclusive scan of the totals over experts (two entries per thread, E <= 1024).
+  // Exclusive scan of the totals over buckets (two entries per thread, <= 1024).
   {
     const int i0 = 2 * tid, i1 = 2 * tid + 1;
     const int v0 = i0 < E ? s_off[i0] : 0;
@@ -150,25 +227,34 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(
 
   if (blockIdx.x == 0) {
     for (int e = tid; e < E; e += kLayoutThreads) {
-      a.counts_e[e] = s_off[e + 1] - s_off[e];
-      a.offsets_e[e] = s_off[e];
+      o.counts[e] = s_off[e + 1] - s_off[e];
+      o.offsets[e] = s_off[e];
     }
-    const int per = E / num_ranks;
-    for (int r = tid; r < num_ranks; r += kLayoutThreads) {
-      a.counts_r[r] = s_off[(r + 1) * per] - s_off[r * per];
-      a.offsets_r[r] = s_off[r * per];
+    if (!kRanks) {
+      const int per = o.per_rank;
+      for (int r = tid; r < o.num_groups; r += kLayoutThreads) {
+        o.group_counts[r] = s_off[(r + 1) * per] - s_off[r * per];
+        o.group_offsets[r] = s_off[r * per];
+      }
     }
     if (tid == 0) {
-      a.offsets_e[E] = s_off[E];
-      a.offsets_r[num_ranks] = s_off[E];
-      a.status[0] = slots - s_off[E];   // skipped (invalid) slots
-      a.status[1] = s_off[E];           // rows in use
-      a.status[2] = slots / (topk > 0 ? topk : 1);
-      a.status[3] = 0;
+      o.offsets[E] = s_off[E];
+      if (!kRanks) o.group_offsets[o.num_groups] = s_off[E];
+      const int num_tokens = b.slots / (b.topk > 0 ? b.topk : 1);
+      if (kRanks) {
+        o.status[0] = s_off[E];           // rows in use: (token, rank) pairs
+        o.status[1] = num_tokens;
+        o.status[2] = 0;
+      } else {
+        o.status[0] = b.slots - s_off[E];  // skipped (invalid) slots
+        o.status[1] = s_off[E];            // rows in use
+        o.status[2] = num_tokens;
+      }
+      o.status[3] = 0;
     }
   }
 
-  // Cursors: expert start + earlier workgroups + earlier wavefronts here.
+  // Cursors: bucket start + earlier workgroups + earlier wavefronts here.
   for (int e = tid; e < E; e += kLayoutThreads) {
     int run = s_off[e] + s_pre[e];
 #pragma unroll
@@ -186,40 +272,72 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(
   for (int s = 0; s < kLayoutSteps; ++s) {
     const int slot = base + s * 64 + lane;
     const int e = ids[s];
-    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
     int p = -1;
-    if (valid) {
+    if (e >= 0) {
       const int c = my_cur[e];
       p = c + static_cast<int>(lanes_below(peers[s]));
       if (lanes_below(peers[s]) == 0) my_cur[e] = c + __popcll(peers[s]);
     }
-    if (slot < slots) {
-      a.pos[slot] = p;
-      if (valid && p < slots) a.src_idx[p] = slot / topk;
+    if (slot < b.slots) {
+      o.pos[slot] = p;
+      if (e >= 0 && p < b.capacity) {
+        const int t = slot / b.topk;
+        o.src[p] = t;
+        if (kRanks) o.rank_pos[static_cast<size_t>(t) * o.num_groups + e] = p;
+      }
     }
   }
 
   // Rows past the valid total hold no token.
   const int total = s_off[E];
-  for (int r = total + blockIdx.x * kLayoutThreads + tid; r < slots; r += nblocks * kLayoutThreads)
-    a.src_idx[r] = -1;
+  for (int r = total + blockIdx.x * kLayoutThreads + tid; r < b.capacity;
+       r += nblocks * kLayoutThreads)
+    o.src[r] = -1;
+}
+
+int bits_for(int n) {
+  int nbits = 0;
+  while ((1 << nbits) < n) ++nbits;
+  return nbits;
+}
+
+template <bool kRanks>
+hipError_t launch_pass(const Buckets& b, const LayoutOut& o, hipStream_t stream) {
+  const int nblocks = layout_blocks(b.slots);
+  hipLaunchKernelGGL(layout_hist_kernel<kRanks>, dim3(nblocks), dim3(kLayoutThreads), 0, stream,
+                     b, o);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(layout_place_kernel<kRanks>, dim3(nblocks), dim3(kLayoutThreads), 0, stream,
+                     b, o);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+// Multiplier that divides by `per` (1 <= per <= 1024) exactly for ids below
+// 1024: floor(e / per) == (e * ceil(2^20 / per)) >> 20 whenever e * per < 2^20.
+uint32_t rank_multiplier(int per) { return ((1u << 20) + per - 1) / per; }
+
 hipError_t launch_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,
                          int num_ranks, const LayoutArrays& a, hipStream_t stream) {
-  const int slots = num_tokens * topk;
-  const int nblocks = layout_blocks(slots);
-  int nbits = 0;
-  while ((1 << nbits) < num_experts) ++nbits;
-  hipLaunchKernelGGL(layout_hist_kernel, dim3(nblocks), dim3(kLayoutThreads), 0, stream, d_idx,
-                     slots, num_experts, nbits, a.hist);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(layout_place_kernel, dim3(nblocks), dim3(kLayoutThreads), 0, stream, d_idx,
-                     slots, topk, num_experts, num_ranks, nbits, a.hist, a);
-  return hipGetLastError();
+  const int per = num_experts / num_ranks;
+  Buckets b{d_idx, num_tokens * topk, topk, num_experts, rank_multiplier(per),
+            num_experts, bits_for(num_experts), num_tokens * topk};
+  LayoutOut o{a.hist, a.counts_e, a.offsets_e, a.counts_r, a.offsets_r, a.pos, a.src_idx,
+              a.status, nullptr, num_ranks, per};
+  return launch_pass<false>(b, o, stream);
+}
+
+hipError_t launch_rank_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,
+                              int num_ranks, const RankArrays& a, hipStream_t stream) {
+  const int per = num_experts / num_ranks;
+  const int rows = num_tokens * (topk < num_ranks ? topk : num_ranks);
+  Buckets b{d_idx, num_tokens * topk, topk, num_experts, rank_multiplier(per),
+            num_ranks, bits_for(num_ranks), rows};
+  LayoutOut o{a.hist, a.counts, a.offsets, nullptr, nullptr, a.slot_row, a.src,
+              a.status, a.rank_pos, num_ranks, per};
+  return launch_pass<true>(b, o, stream);
 }
 
 }  // namespace moe

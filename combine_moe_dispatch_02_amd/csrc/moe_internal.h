@@ -38,9 +38,23 @@ struct LayoutArrays {
   int32_t* src_idx;    // [T_max * k]
 };
 
+// Workspace regions of the rank-deduplicated layout.
+struct RankArrays {
+  int32_t* status;    // [MOE_EP_STATUS_WORDS]
+  int32_t* counts;    // [R] tokens per rank
+  int32_t* offsets;   // [R + 1]
+  int32_t* hist;      // [layout_blocks(T_max * k)][R]
+  int32_t* slot_row;  // [T_max * k] row of the (token, rank) pair a slot opens, else -1
+  int32_t* rank_pos;  // [T_max * R] row of each (token, rank) pair, -1 if none
+  int32_t* src;       // [T_max * min(k, R)] token of each row
+};
+
 // Host-side launchers; each returns the hipError_t of its launches.
 hipError_t launch_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,
                          int num_ranks, const LayoutArrays& a, hipStream_t stream);
+
+hipError_t launch_rank_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,
+                              int num_ranks, const RankArrays& a, hipStream_t stream);
 
 // `rows` is the row count of the expert-major buffer; rows outside it are
 // never read or written, whatever pos holds.
@@ -70,5 +84,13 @@ inline dim3 item_grid(int64_t num_items, int max_blocks) {
   if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
   return dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks));
 }
+
+hipError_t launch_rank_meta(const int32_t* d_idx, const float* d_w, const int32_t* d_slot_row,
+                            int num_tokens, int topk, int num_experts, int num_ranks, int64_t rows,
+                            int32_t* d_recv_idx, float* d_recv_w, hipStream_t stream);
+
+hipError_t launch_combine_ranks(const void* d_y, int64_t rows, const int32_t* d_rank_pos,
+                                void* d_out, int num_tokens, int num_ranks, int hidden,
+                                int max_blocks, hipStream_t stream);
 
 }  // namespace moe

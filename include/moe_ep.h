@@ -148,8 +148,61 @@ int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, float*
 int moe_combine(moe_handle_t h, const void* d_y, int64_t y_rows, const float* d_w, void* d_out,
                 hipStream_t stream);
 
-/* Cap the number of workgroups (of 4 wavefronts each) that moe_dispatch and
- * moe_combine launch; 0 (the default) launches one workgroup per 4 work items.
+/* ---- Rank-deduplicated exchange --------------------------------------------
+ * What an expert-parallel exchange carries ("Inside the Nebius + PyTorch
+ * DeepSeek V3 recipe", section "Mixture-of-experts and wide expert
+ * parallelism": each rank holds a subset of the experts): a token routed to
+ * several experts on one rank is sent to that rank once. Rows are grouped by
+ * virtual rank, tokens in token order within a rank; capacity (the worst
+ * case) is num_tokens * min(topk, R) rows. Each row carries the token's k
+ * slots as the receiving rank numbers its experts (e - r*E/R, or -1 for a
+ * slot whose expert is on another rank) and the slot weights (0 where -1),
+ * so a receiver expands its rows to its experts with moe_dispatch_layout +
+ * moe_dispatch on a handle with E/R experts and 1 rank (the -1 slots are
+ * skipped), reduces them locally with moe_combine, and the source adds the
+ * per-rank partial rows with moe_combine_ranks. */
+
+typedef struct {
+  int32_t* rank_pos;  /* [num_tokens, R] row of each (token, rank) pair, -1 if none */
+  int32_t* slot_row;  /* [num_tokens * topk] row a slot opens (first slot of its token on
+                         that rank), else -1 */
+  int32_t* src_idx;   /* [capacity] token of each row, -1 past the valid total */
+  int32_t* counts_r;  /* [R] tokens per rank */
+  int32_t* offsets_r; /* [R + 1] */
+  int32_t* status;    /* [MOE_EP_STATUS_WORDS]; [0] = rows in use, [1] = num_tokens */
+  int32_t num_tokens;
+  int64_t capacity;   /* num_tokens * min(topk, R) */
+} moe_rank_layout_view_t;
+
+/* Rank layout: which ranks each token goes to and the row of every
+ * (token, rank) pair (histogram, exclusive scan, stable placement over the
+ * R ranks). Same arguments and conventions as moe_dispatch_layout; uses its
+ * own workspace regions, so both layouts can coexist. */
+int moe_rank_layout(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_tokens,
+                    hipStream_t stream);
+
+/* Device pointers and sizes of the last rank layout (MOE_ERR_STATE before one). */
+int moe_rank_layout_view(moe_handle_t h, moe_rank_layout_view_t* out);
+
+/* Send side of the exchange: row rank_pos[t, r] receives x[t] (bf16 [num_tokens,
+ * hidden]) for every rank r the token reaches, plus the receiver metadata
+ * recv_idx int32 [out_rows, topk] and recv_w fp32 [out_rows, topk].
+ * d_topk_idx / d_w: the same int32 / fp32 [num_tokens, topk] the rank layout
+ * was built from. out_rows >= capacity; rows past the valid total are not
+ * written. Requires a rank layout (MOE_ERR_STATE otherwise). */
+int moe_dispatch_ranks(moe_handle_t h, const void* d_x, const int32_t* d_topk_idx,
+                       const float* d_w, void* d_out, int32_t* d_recv_idx, float* d_recv_w,
+                       int64_t out_rows, hipStream_t stream);
+
+/* Source side of the return trip: out[t] = bf16_rne(sum over ranks r in
+ * ascending order of y[rank_pos[t, r]]), fp32 accumulation; y bf16 [y_rows,
+ * hidden] holds each (token, rank) row's partial result, y_rows >= capacity;
+ * out bf16 [num_tokens, hidden]. */
+int moe_combine_ranks(moe_handle_t h, const void* d_y, int64_t y_rows, void* d_out,
+                      hipStream_t stream);
+
+/* Cap the number of workgroups (of 4 wavefronts each) that the dispatch and
+ * combine calls launch; 0 (the default) launches one workgroup per 4 work items.
  * With a cap, each wavefront loops over several (token, column slice) items,
  * so the work occupies fewer compute units and leaves the rest free for
  * kernels on other streams -- the pages' point that the exchange should fill

@@ -9,12 +9,15 @@ Contents:
   * ``codecs``  -- bf16 and OCP FP8 E4M3 encoders/decoders written from the
     formats' definitions (nearest representable value, ties to even).
   * ``moe``     -- layout (histogram, exclusive scan, stable placement),
-    bf16 dispatch, FP8 dispatch with per-128-channel scales, combine, and the
-    expert-side FP8 dequantisation used by the tests.
+    bf16 dispatch, FP8 dispatch with per-128-channel scales, combine, the
+    expert-side FP8 dequantisation used by the tests, and the
+    rank-deduplicated exchange (rank layout, dispatch with receiver
+    metadata, combine of per-rank partial rows).
 
 Every function is pinned by ``tests/test_oracle_*.py`` against library
 routines, closed forms, invariants, brute force on tiny inputs and the
 hand-worked fixtures under ``tests/golden/``.
 """
 from . import codecs, moe  # noqa: F401
-from .moe import layout, dispatch_bf16, dispatch_fp8, combine, dequant_fp8  # noqa: F401
+from .moe import (layout, dispatch_bf16, dispatch_fp8, combine, dequant_fp8,  # noqa: F401
+                  rank_layout, dispatch_ranks, combine_ranks)

@@ -39,7 +39,7 @@ import numpy as np
 from .codecs import bf16_decode, bf16_encode, e4m3_decode, e4m3_encode
 
 __all__ = ["layout", "dispatch_bf16", "dispatch_fp8", "combine", "dequant_fp8",
-           "FP8_BLOCK", "FP8_MAX"]
+           "rank_layout", "dispatch_ranks", "combine_ranks", "FP8_BLOCK", "FP8_MAX"]
 
 FP8_BLOCK = 128
 FP8_MAX = np.float32(448.0)
@@ -188,3 +188,109 @@ def dequant_fp8(codes, scales) -> np.ndarray:
     vals = e4m3_decode(codes).reshape(C, H // FP8_BLOCK, FP8_BLOCK)
     prod = vals * scales.astype(np.float64)[:, :, None]                # exact in fp64
     return bf16_encode(prod.reshape(C, H))
+
+
+# ---------------------------------------------------------------------------
+# Rank-deduplicated exchange: one row per (token, destination rank).
+#
+# What an expert-parallel exchange carries ("Inside the Nebius + PyTorch
+# DeepSeek V3 recipe", section "Mixture-of-experts and wide expert
+# parallelism": each rank holds a subset of the experts, dispatch sends
+# tokens to the ranks holding their experts): a token routed to several
+# experts of one rank travels to that rank once. Readings (the pages give no
+# formula): ranks own contiguous experts; a rank's rows are its tokens in
+# token order; each row carries the token's k slots re-expressed for the
+# receiver -- the local expert id (e - r*E/R) where the slot's expert lives
+# on rank r, else -1 -- and the slot weights (0 where not local); combine
+# adds the per-rank partial rows in ascending rank order and rounds once.
+
+
+def rank_layout(topk_idx, num_experts: int, num_ranks: int) -> dict:
+    """Which ranks each token goes to, and the rank-major row of each pair.
+
+    Returns int64 arrays: in_rank [T, R] (0/1), counts_r [R], offsets_r
+    [R+1], rank_pos [T, R] (row, or -1), rank_src [T*min(k, R)] (token of
+    each row, -1 past the valid total).
+    """
+    idx = np.asarray(topk_idx)
+    T, k = idx.shape
+    E, R = int(num_experts), int(num_ranks)
+    if E <= 0 or R <= 0 or E % R != 0:
+        raise ValueError("num_experts must be a positive multiple of num_ranks")
+    per = E // R
+    rows = idx.tolist()
+    in_rank = [[0] * R for _ in range(T)]
+    for t in range(T):
+        for j in range(k):
+            e = rows[t][j]
+            if 0 <= e < E:
+                in_rank[t][e // per] = 1
+    counts = [sum(in_rank[t][r] for t in range(T)) for r in range(R)]
+    offsets = [0] * (R + 1)
+    for r in range(R):
+        offsets[r + 1] = offsets[r] + counts[r]
+    cursor = offsets[:R]
+    rank_pos = [[-1] * R for _ in range(T)]
+    rank_src = [-1] * (T * min(k, R))
+    for t in range(T):
+        for r in range(R):
+            if in_rank[t][r]:
+                p = cursor[r]
+                cursor[r] = p + 1
+                rank_pos[t][r] = p
+                rank_src[p] = t
+    as64 = lambda a: np.asarray(a, dtype=np.int64)  # noqa: E731
+    return {"in_rank": as64(in_rank).reshape(T, R), "counts_r": as64(counts),
+            "offsets_r": as64(offsets), "rank_pos": as64(rank_pos).reshape(T, R),
+            "rank_src": as64(rank_src)}
+
+
+def dispatch_ranks(x_bits, topk_idx, topk_w, num_experts: int, num_ranks: int, rl: dict):
+    """Rank-deduplicated bf16 dispatch with the receiver's routing metadata.
+
+    Returns (rows uint16 [T*min(k,R), H], recv_idx int64 [same rows, k],
+    recv_w float32 [same rows, k]); unused rows are zero / -1 / 0.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    idx = np.asarray(topk_idx)
+    w = np.asarray(topk_w, dtype=np.float32)
+    T, k = idx.shape
+    E, R = int(num_experts), int(num_ranks)
+    per = E // R
+    cap = T * min(k, R)
+    out = np.zeros((cap, x_bits.shape[1]), dtype=np.uint16)
+    recv_idx = np.full((cap, k), -1, dtype=np.int64)
+    recv_w = np.zeros((cap, k), dtype=np.float32)
+    for t in range(T):
+        for r in range(R):
+            p = int(rl["rank_pos"][t, r])
+            if p < 0:
+                continue
+            out[p] = x_bits[t]
+            for j in range(k):
+                e = int(idx[t, j])
+                if 0 <= e < E and e // per == r:
+                    recv_idx[p, j] = e - r * per
+                    recv_w[p, j] = w[t, j]
+    return out, recv_idx, recv_w
+
+
+def combine_ranks(partial_bits, rank_pos, tokens=None, return_magnitude: bool = False):
+    """out[t] = bf16( sum over ranks r in ascending order of partial[rank_pos[t, r]] ),
+    summed in fp64 and rounded once; tokens with no rank get zeros. With
+    ``return_magnitude`` also returns sum_r |partial[rank_pos[t, r]]|."""
+    partial_bits = np.asarray(partial_bits, dtype=np.uint16)
+    rank_pos = np.asarray(rank_pos)
+    T, R = rank_pos.shape
+    toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    acc = np.zeros((toks.shape[0], partial_bits.shape[1]), dtype=np.float64)
+    mag = np.zeros_like(acc)
+    for r in range(R):
+        p = rank_pos[toks, r]
+        ok = p >= 0
+        rows = bf16_decode(partial_bits[np.where(ok, p, 0)]).astype(np.float64)
+        rows[~ok] = 0.0
+        acc += rows
+        mag += np.abs(rows)
+    out = bf16_encode(acc)
+    return (out, mag) if return_magnitude else out

@@ -52,9 +52,10 @@ def test_workspace_bytes(lib):
     c = cfg(4096, 7168, 8, 256, 8)
     n = lib.moe_workspace_bytes(ctypes.byref(c))
     slots = 4096 * 8
-    # pos + src_idx + 16 layout histograms of 256 experts + small arrays
-    assert n >= 2 * 4 * slots + 16 * 256 * 4
-    assert n < 2 * 4 * slots + 16 * 256 * 4 + 16 * 1024
+    # expert layout: pos + src_idx + 16 histograms of 256 experts; rank layout:
+    # slot_row + rank_pos [T, 8] + src [T * 8] + 16 histograms of 8 ranks; small arrays
+    need = 2 * 4 * slots + 16 * 256 * 4 + 4 * slots + 4 * 4096 * 8 + 4 * 4096 * 8 + 16 * 8 * 4
+    assert need <= n < need + 16 * 1024
     assert n % 256 == 0
     zero = lib.moe_workspace_bytes(ctypes.byref(cfg(0)))
     assert zero > 0
@@ -125,6 +126,20 @@ def test_layout_argument_errors(lib):
     assert lib.moe_dispatch_layout(h, None, 5, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_layout(h, ctypes.c_void_p((1 << 24) + 2), 5, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_layout(None, fake, 5, None) == _lib.MOE_ERR_INVALID_ARG
+    lib.moe_handle_destroy(h)
+
+
+def test_rank_calls_need_a_rank_layout(lib):
+    h = make_handle(lib)
+    fake = ctypes.c_void_p(1 << 24)
+    assert lib.moe_dispatch_ranks(h, fake, fake, fake, fake, fake, fake, 1 << 10, None) == _lib.MOE_ERR_STATE
+    assert "moe_rank_layout" in lib.moe_last_error().decode()
+    assert lib.moe_combine_ranks(h, fake, 1 << 10, fake, None) == _lib.MOE_ERR_STATE
+    v = _lib.MoeRankLayoutView()
+    assert lib.moe_rank_layout_view(h, ctypes.byref(v)) == _lib.MOE_ERR_STATE
+    assert lib.moe_rank_layout(h, fake, 129, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_rank_layout(h, None, 3, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_rank_layout(None, fake, 3, None) == _lib.MOE_ERR_INVALID_ARG
     lib.moe_handle_destroy(h)
 
 
