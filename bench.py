@@ -38,6 +38,12 @@ def op_bytes(T, H, k):
     }
 
 
+def mxfp8_bytes(T, H, k):
+    """MXFP8 dispatch (not part of the step): x once, codes + E8M0 bytes per row, pos."""
+    S = T * k
+    return 2 * T * H + S * H + S * (H // 32) + 4 * S
+
+
 KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_kernel", "dispatch_fp8": "dispatch_fp8_kernel",
                 "combine": "combine_kernel"}
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -232,6 +238,27 @@ def main():
             sustained[label] = {"bytes": moved, "us_median": round(float(np.median(us)), 2),
                                 "GBps": round(moved / (np.median(us) * 1e-6) / 1e9, 1)}
         del bufs
+        # MXFP8 dispatch (32-channel blocks, E8M0 scales), same method.
+        for b in sets:
+            b["mx_scales"] = torch.empty((S, H // 32), dtype=torch.uint8, device=dev)
+        mx = mxfp8_bytes(T, H, k)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.sustained_iters)]
+        h.layout(sets[0]["idx"])
+        for i in range(3 + args.sustained_iters):
+            b = sets[i % len(sets)]
+            if i >= 3:
+                evs[i - 3][0].record(stream)
+            h.dispatch(b["x"], mxfp8=True, out=b["q_out"], scales=b["mx_scales"])
+            if i >= 3:
+                evs[i - 3][1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(e) * 1e3 for a, e in evs]))
+        sustained["dispatch_mxfp8"] = {"bytes": mx, "us_median": round(us, 2),
+                                       "GBps": round(mx / (us * 1e-6) / 1e9, 1),
+                                       "frac_of_peak": round(mx / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        for b in sets:
+            del b["mx_scales"]
 
     # Rank-deduplicated exchange (one row per (token, rank)), sustained method.
     exchange = {}

@@ -15,7 +15,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_EP_FP8_BLOCK, MOE_EP_MAX_EXPERTS,
+from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP8_E4M3, MOE_MX_BLOCK,
+                   MOE_EP_FP8_BLOCK, MOE_EP_MAX_EXPERTS,
                    MOE_EP_MAX_TOPK, MOE_EP_STATUS_WORDS, MoeConfig, MoeError, MoeLayoutView,
                    MoeRankLayoutView)
 
@@ -23,7 +24,7 @@ __all__ = ["Handle", "MoeError", "MoeConfig", "moe_workspace_bytes", "moe_handle
            "moe_handle_destroy", "moe_dispatch_layout", "moe_layout_view", "moe_dispatch",
            "moe_combine", "moe_rank_layout", "moe_rank_layout_view", "moe_dispatch_ranks",
            "moe_combine_ranks", "moe_set_max_workgroups", "moe_status_string", "moe_last_error",
-           "MOE_DTYPE_BF16",
+           "MOE_DTYPE_BF16", "MOE_DTYPE_MXFP8_E4M3",
            "MOE_DTYPE_FP8_E4M3", "MOE_EP_MAX_EXPERTS", "MOE_EP_MAX_TOPK", "MOE_EP_FP8_BLOCK"]
 
 
@@ -95,7 +96,11 @@ def moe_dispatch(h: int, x: torch.Tensor, dtype: int, out: torch.Tensor,
     px = _ptr(x, torch.bfloat16, "x")
     want = torch.bfloat16 if dtype == MOE_DTYPE_BF16 else torch.uint8
     po = _ptr(out, want, "out")
-    ps = _ptr(scales, torch.float32, "scales") if dtype == MOE_DTYPE_FP8_E4M3 else None
+    ps = None
+    if dtype == MOE_DTYPE_FP8_E4M3:
+        ps = _ptr(scales, torch.float32, "scales")
+    elif dtype == MOE_DTYPE_MXFP8_E4M3:
+        ps = _ptr(scales, torch.uint8, "scales")
     _lib.check(_lib.load().moe_dispatch(ctypes.c_void_p(h), ctypes.c_void_p(px), int(dtype),
                                         ctypes.c_void_p(po), ctypes.c_void_p(ps),
                                         out.shape[0], _stream(stream, x.device)))
@@ -234,10 +239,20 @@ class Handle:
     def capacity(self) -> int:
         return self.num_tokens * self.topk
 
-    def dispatch(self, x: torch.Tensor, fp8: bool = False, out=None, scales=None, stream=None):
-        """bf16 rows -> [capacity, H] bf16, or (uint8 codes, fp32 scales) with fp8."""
+    def dispatch(self, x: torch.Tensor, fp8: bool = False, out=None, scales=None, stream=None,
+                 mxfp8: bool = False):
+        """bf16 rows -> [capacity, H] bf16; (uint8 codes, fp32 scales [., H/128]) with
+        fp8; (uint8 codes, uint8 E8M0 scales [., H/32]) with mxfp8."""
         _ptr(x, torch.bfloat16, "x", self.device)
         rows = self.capacity
+        if mxfp8:
+            if out is None:
+                out = torch.empty((rows, self.hidden), dtype=torch.uint8, device=self.device)
+            if scales is None:
+                scales = torch.empty((rows, self.hidden // MOE_MX_BLOCK), dtype=torch.uint8,
+                                     device=self.device)
+            moe_dispatch(self.h, x, MOE_DTYPE_MXFP8_E4M3, out, scales, stream)
+            return out, scales
         if fp8:
             if out is None:
                 out = torch.empty((rows, self.hidden), dtype=torch.uint8, device=self.device)

@@ -13,6 +13,8 @@ MOE_ERR_STATE = 3
 MOE_ERR_HIP = 4
 MOE_DTYPE_BF16 = 0
 MOE_DTYPE_FP8_E4M3 = 1
+MOE_DTYPE_MXFP8_E4M3 = 2
+MOE_MX_BLOCK = 32
 MOE_EP_MAX_EXPERTS = 1024
 MOE_EP_MAX_TOPK = 32
 MOE_EP_FP8_BLOCK = 128

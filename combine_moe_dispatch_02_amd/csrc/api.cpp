@@ -250,22 +250,21 @@ int moe_layout_view(moe_handle_t h, moe_layout_view_t* out) {
   return ok();
 }
 
-int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, float* d_scales,
+int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, void* d_scales,
                  int64_t out_rows, hipStream_t stream) {
   const int st = check_ready(h, "moe_dispatch");
   if (st != MOE_OK) return st;
   const int64_t capacity = int64_t(h->num_tokens) * h->cfg.topk;
-  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3)
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3 && dtype != MOE_DTYPE_MXFP8_E4M3)
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: unknown dtype %d", dtype);
   if (out_rows < capacity)
     return fail(MOE_ERR_INVALID_ARG,
                 "moe_dispatch: out_rows=%lld is below the worst-case capacity num_tokens*topk=%lld",
                 (long long)out_rows, (long long)capacity);
-  if (dtype == MOE_DTYPE_FP8_E4M3 && h->cfg.hidden % MOE_EP_FP8_BLOCK != 0)
+  if (dtype != MOE_DTYPE_BF16 && h->cfg.hidden % MOE_EP_FP8_BLOCK != 0)
     return fail(MOE_ERR_UNSUPPORTED,
-                "moe_dispatch: FP8 needs hidden to be a multiple of %d (one scale per %d "
-                "channels); hidden=%d",
-                MOE_EP_FP8_BLOCK, MOE_EP_FP8_BLOCK, h->cfg.hidden);
+                "moe_dispatch: FP8 and MXFP8 need hidden to be a multiple of %d; hidden=%d",
+                MOE_EP_FP8_BLOCK, h->cfg.hidden);
   if (h->num_tokens == 0) return ok();
   if (d_x == nullptr || d_out == nullptr)
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: x or out is NULL");
@@ -280,9 +279,14 @@ int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, float*
       return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: FP8 dispatch needs a scales buffer");
     if (!aligned(d_scales, 4))
       return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: scales must be 4-byte aligned");
-    err = moe::launch_dispatch_fp8(d_x, h->arrays.pos, d_out, d_scales, out_rows,
-                                   h->num_tokens, h->cfg.topk, h->cfg.hidden, h->max_workgroups,
-                                   stream);
+    if (dtype == MOE_DTYPE_FP8_E4M3)
+      err = moe::launch_dispatch_fp8(d_x, h->arrays.pos, d_out, static_cast<float*>(d_scales),
+                                     out_rows, h->num_tokens, h->cfg.topk, h->cfg.hidden,
+                                     h->max_workgroups, stream);
+    else
+      err = moe::launch_dispatch_mxfp8(d_x, h->arrays.pos, d_out, d_scales, out_rows,
+                                       h->num_tokens, h->cfg.topk, h->cfg.hidden,
+                                       h->max_workgroups, stream);
   }
   return hip_status(err, "moe_dispatch");
 }

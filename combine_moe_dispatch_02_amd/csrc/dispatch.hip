@@ -143,6 +143,79 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_fp8_kernel(
   }
 }
 
+// MXFP8 (OCP Microscaling v1.0, E4M3 elements): 32-channel blocks share an
+// E8M0 power-of-two scale. A lane holds 16 channels, so a block is a lane
+// pair; shared = floor(log2 amax) - 8 (8: exponent of E4M3's largest normal),
+// clamped to E8M0's [-127, 127], read off amax's fp32 bit fields. Elements are
+// x * 2^-shared (exact: a power of two, and every product that can round to a
+// nonzero code is a normal fp32), clamped to +-448 and converted by the
+// hardware fp32 -> fp8 instruction (round-to-nearest-even). An all-zero block
+// gets code 0 and signed-zero elements. Four E8M0 bytes go out per dword
+// store. The Hybrid-EP news item ("Efficiency Numbers") reports its Qwen3 run
+// in MXFP8.
+__global__ __launch_bounds__(64 * kItemWaves) void dispatch_mxfp8_kernel(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ out,
+    uint32_t* __restrict__ scales, int num_tokens, int topk, int hidden, int slices, int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int units = hidden >> 4;           // 16 channels per lane
+  const int scale_words = hidden >> 7;     // 4 one-byte scales per dword, per row
+  const int nitems = num_tokens * slices;
+  for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
+       item += gridDim.x * kItemWaves) {
+    const int t = item / slices;
+    const int u = (item - t * slices) * 64 + lane;
+    // units is a multiple of 8, so each 8-lane group is wholly active or not.
+    const bool active = u < units;
+    const u32x4* src = x + static_cast<size_t>(t) * (hidden >> 3);
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (active) {
+      a = src[2 * u];
+      b = src[2 * u + 1];
+    }
+    float f[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
+                   bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
+                   bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
+                   bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(f[i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    const uint32_t mb = __float_as_uint(m);
+    int shared = -127;
+    if (mb != 0u) {
+      const int fl = mb >= 0x00800000u ? static_cast<int>(mb >> 23) - 127   // normal
+                                       : 31 - __clz(mb) - 149;                // subnormal
+      shared = fl - 8 < -127 ? -127 : (fl - 8 > 127 ? 127 : fl - 8);
+    }
+    const float inv = __uint_as_float(static_cast<uint32_t>(127 - shared) << 23);   // 2^-shared
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[i] = __builtin_amdgcn_fmed3f(f[i] * inv, -448.0f, 448.0f);
+    u32x4 q;
+    q.x = pack_e4m3(f[0], f[1], f[2], f[3]);
+    q.y = pack_e4m3(f[4], f[5], f[6], f[7]);
+    q.z = pack_e4m3(f[8], f[9], f[10], f[11]);
+    q.w = pack_e4m3(f[12], f[13], f[14], f[15]);
+    // Lane 8i gathers the codes of blocks u/2 .. u/2+3 (lanes 8i, 8i+2, 8i+4, 8i+6).
+    const uint32_t code = static_cast<uint32_t>(shared + 127);
+    const uint32_t c1 = __shfl(code, lane + 2, 64);
+    const uint32_t c2 = __shfl(code, lane + 4, 64);
+    const uint32_t c3 = __shfl(code, lane + 6, 64);
+    const uint32_t word = code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    const bool scale_lane = active && (lane & 7) == 0;
+    const int32_t* pt = pos + static_cast<size_t>(t) * topk;
+    for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
+      int p[kSlotBatch];
+      load_rows(pt, j0, topk, rows, p);
+#pragma unroll
+      for (int jj = 0; jj < kSlotBatch; ++jj) {
+        if (p[jj] < 0) continue;
+        if (active) out[static_cast<size_t>(p[jj]) * units + u] = q;
+        if (scale_lane) scales[static_cast<size_t>(p[jj]) * scale_words + (u >> 3)] = word;
+      }
+    }
+  }
+}
+
 // Receiver metadata of the rank-deduplicated exchange. One thread per slot
 // (t, j): for each (token, rank) row p of token t (opened by slot jr), entry
 // (p, j) says whether slot j's expert lives on that row's rank -- its local id
@@ -169,6 +242,19 @@ __global__ __launch_bounds__(256) void rank_meta_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_dispatch_mxfp8(const void* d_x, const int32_t* d_pos, void* d_out,
+                                 void* d_scales, int64_t rows, int num_tokens, int topk,
+                                 int hidden, int max_blocks, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int units = hidden / 16;
+  const int slices = (units + 63) / 64;
+  hipLaunchKernelGGL(dispatch_mxfp8_kernel, item_grid(int64_t(num_tokens) * slices, max_blocks),
+                     dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_x), d_pos,
+                     static_cast<u32x4*>(d_out), static_cast<uint32_t*>(d_scales), num_tokens,
+                     topk, hidden, slices, rows);
+  return hipGetLastError();
+}
 
 hipError_t launch_rank_meta(const int32_t* d_idx, const float* d_w, const int32_t* d_slot_row,
                             int num_tokens, int topk, int num_experts, int num_ranks, int64_t rows,

@@ -85,6 +85,10 @@ inline dim3 item_grid(int64_t num_items, int max_blocks) {
   return dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks));
 }
 
+hipError_t launch_dispatch_mxfp8(const void* d_x, const int32_t* d_pos, void* d_out,
+                                 void* d_scales, int64_t rows, int num_tokens, int topk,
+                                 int hidden, int max_blocks, hipStream_t stream);
+
 hipError_t launch_rank_meta(const int32_t* d_idx, const float* d_w, const int32_t* d_slot_row,
                             int num_tokens, int topk, int num_experts, int num_ranks, int64_t rows,
                             int32_t* d_recv_idx, float* d_recv_w, hipStream_t stream);

@@ -77,8 +77,9 @@ typedef enum {
 } moe_status_t;
 
 typedef enum {
-  MOE_DTYPE_BF16 = 0,    /* payload rows are bf16, copied bit for bit */
-  MOE_DTYPE_FP8_E4M3 = 1 /* payload rows are E4M3 bytes + fp32 scales */
+  MOE_DTYPE_BF16 = 0,      /* payload rows are bf16, copied bit for bit */
+  MOE_DTYPE_FP8_E4M3 = 1,  /* E4M3 bytes + one fp32 scale per 128 channels */
+  MOE_DTYPE_MXFP8_E4M3 = 2 /* OCP MX: E4M3 bytes + one E8M0 byte per 32 channels */
 } moe_dtype_t;
 
 /* Fixed at handle creation. max_tokens bounds num_tokens of every layout. */
@@ -134,11 +135,17 @@ int moe_layout_view(moe_handle_t h, moe_layout_view_t* out);
 
 /* Dispatch: scatter token rows into the expert-major buffer.
  * d_x: bf16 [num_tokens, hidden]. out_rows >= capacity of the last layout.
- *   MOE_DTYPE_BF16:     d_out bf16 [out_rows, hidden], d_scales ignored;
- *   MOE_DTYPE_FP8_E4M3: d_out uint8 [out_rows, hidden], d_scales fp32
- *                       [out_rows, hidden / 128] (hidden % 128 == 0).
+ *   MOE_DTYPE_BF16:       d_out bf16 [out_rows, hidden], d_scales ignored;
+ *   MOE_DTYPE_FP8_E4M3:   d_out uint8 [out_rows, hidden], d_scales fp32
+ *                         [out_rows, hidden / 128] (hidden % 128 == 0);
+ *   MOE_DTYPE_MXFP8_E4M3: d_out uint8 [out_rows, hidden], d_scales uint8 E8M0
+ *                         [out_rows, hidden / 32] (hidden % 128 == 0; OCP
+ *                         Microscaling v1.0: shared exponent floor(log2
+ *                         amax) - 8 clamped to [-127, 127], elements E4M3
+ *                         nearest-even of x / 2^shared clamped to +-448;
+ *                         an all-zero block has code 0).
  * Row pos[t*k+j] receives token t; rows past the valid total are not written. */
-int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, float* d_scales,
+int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, void* d_scales,
                  int64_t out_rows, hipStream_t stream);
 
 /* Combine: top-k weighted gather back to token order.

@@ -12,7 +12,8 @@ Contents:
     bf16 dispatch, FP8 dispatch with per-128-channel scales, combine, the
     expert-side FP8 dequantisation used by the tests, and the
     rank-deduplicated exchange (rank layout, dispatch with receiver
-    metadata, combine of per-rank partial rows).
+    metadata, combine of per-rank partial rows), and MXFP8 dispatch (OCP MX
+    v1.0: 32-element blocks, E8M0 power-of-two scales, E4M3 elements).
 
 Every function is pinned by ``tests/test_oracle_*.py`` against library
 routines, closed forms, invariants, brute force on tiny inputs and the
@@ -20,4 +21,4 @@ hand-worked fixtures under ``tests/golden/``.
 """
 from . import codecs, moe  # noqa: F401
 from .moe import (layout, dispatch_bf16, dispatch_fp8, combine, dequant_fp8,  # noqa: F401
-                  rank_layout, dispatch_ranks, combine_ranks)
+                  rank_layout, dispatch_ranks, combine_ranks, dispatch_mxfp8, dequant_mxfp8)

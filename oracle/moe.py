@@ -39,10 +39,13 @@ import numpy as np
 from .codecs import bf16_decode, bf16_encode, e4m3_decode, e4m3_encode
 
 __all__ = ["layout", "dispatch_bf16", "dispatch_fp8", "combine", "dequant_fp8",
-           "rank_layout", "dispatch_ranks", "combine_ranks", "FP8_BLOCK", "FP8_MAX"]
+           "rank_layout", "dispatch_ranks", "combine_ranks", "quantize_mxfp8_rows",
+           "dispatch_mxfp8", "dequant_mxfp8", "e8m0_decode", "FP8_BLOCK", "FP8_MAX", "MX_BLOCK"]
 
 FP8_BLOCK = 128
 FP8_MAX = np.float32(448.0)
+MX_BLOCK = 32
+E4M3_EMAX = 8          # exponent of E4M3's largest normal value, 448 = 1.75 * 2^8
 
 
 def layout(topk_idx, num_experts: int, num_ranks: int) -> dict:
@@ -294,3 +297,60 @@ def combine_ranks(partial_bits, rank_pos, tokens=None, return_magnitude: bool = 
         mag += np.abs(rows)
     out = bf16_encode(acc)
     return (out, mag) if return_magnitude else out
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 dispatch: OCP Microscaling (MX) v1.0 format with E4M3 elements.
+#
+# The Hybrid-EP news item ("Efficiency Numbers") reports its Qwen3 run in
+# MXFP8. The MX format (OCP Microscaling Formats specification v1.0): blocks
+# of 32 elements share one E8M0 scale (an 8-bit power-of-two exponent, bias
+# 127, no sign or mantissa); its conversion rule takes the shared exponent
+# floor(log2(max |V|)) - emax_elem (emax_elem = 8 for E4M3), divides each
+# element by 2^shared (exact: a power of two) and rounds it to the element
+# format to nearest-even, clamping magnitudes above the largest normal (448).
+# Readings (the pages give none): the shared exponent is clamped to E8M0's
+# finite range [-127, 127]; an all-zero block gets code 0 (2^-127) and
+# signed-zero elements.
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """E8M0 scale codes -> float64 powers of two (0xFF is NaN)."""
+    c = np.asarray(codes).astype(np.int64)
+    v = np.ldexp(1.0, c - 127)
+    return np.where(c == 255, np.nan, v)
+
+
+def quantize_mxfp8_rows(x_bits):
+    """Per-token MXFP8 quantisation: (codes uint8 [T, H], scales uint8 [T, H/32])."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, H = x_bits.shape
+    if H % MX_BLOCK != 0:
+        raise ValueError("hidden must be a multiple of 32 for MXFP8 dispatch")
+    xf = bf16_decode(x_bits).astype(np.float64).reshape(T, H // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(xf), axis=2)
+    nonzero = amax > 0
+    _, e = np.frexp(np.where(nonzero, amax, 1.0))        # amax = m * 2^e, m in [0.5, 1)
+    shared = np.clip(e - 1 - E4M3_EMAX, -127, 127)
+    shared = np.where(nonzero, shared, -127)
+    q = xf / np.ldexp(1.0, shared)[:, :, None]           # exact: division by 2^shared
+    q = np.clip(q, -448.0, 448.0)
+    codes = e4m3_encode(q).reshape(T, H)
+    return codes, (shared + 127).astype(np.uint8)
+
+
+def dispatch_mxfp8(x_bits, pos):
+    """MXFP8 dispatch: quantise each token once, write codes + E8M0 scales to its rows."""
+    pos = np.asarray(pos)
+    T, k = pos.shape
+    codes, scale = quantize_mxfp8_rows(x_bits)
+    return (_scatter_rows(codes, pos, T * k, 0), _scatter_rows(scale, pos, T * k, 0))
+
+
+def dequant_mxfp8(codes, scales) -> np.ndarray:
+    """bf16(code value * 2^(scale - 127)) (exact product, one rounding)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    C, H = codes.shape
+    vals = e4m3_decode(codes).reshape(C, H // MX_BLOCK, MX_BLOCK)
+    prod = vals * e8m0_decode(scales)[:, :, None]
+    return bf16_encode(prod.reshape(C, H))

@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
         m = re.search(rf"#define {name} (\d+)", text)
         assert m and int(m.group(1)) == getattr(_lib, name)
     for name in ("MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_STATE", "MOE_ERR_HIP",
-                 "MOE_DTYPE_BF16", "MOE_DTYPE_FP8_E4M3"):
+                 "MOE_DTYPE_BF16", "MOE_DTYPE_FP8_E4M3", "MOE_DTYPE_MXFP8_E4M3"):
         m = re.search(rf"\b{name} = (\d+)", text)
         assert m and int(m.group(1)) == getattr(_lib, name), name
 

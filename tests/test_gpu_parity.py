@@ -1,7 +1,7 @@
 """GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
 
-Bar: layout arrays, dispatched bf16 rows, FP8 codes and fp32 scales are
-bit-exact; combine is within 1e-2 relative error (plus the fp32 cancellation
+Bar: layout arrays, dispatched bf16 rows, FP8 codes and fp32 scales, MXFP8
+codes and E8M0 scales are bit-exact; combine is within 1e-2 relative error (plus the fp32 cancellation
 term derived in conftest.combine_tolerance). Workloads are the five seeded
 shapes at full size, plus edge cases (empty, one token, k=1, one expert per
 rank, every slot on one expert, invalid ids, the maximum E and k, 65536
@@ -104,6 +104,11 @@ def test_edge_cases_all_ops(case):
     rc, rs = oracle.dispatch_fp8(xb, ref["pos"])
     assert np.array_equal(host_bits(codes)[:total], rc[:total])
     assert np.array_equal(host_bits(scales)[:total].view(np.uint32), rs[:total].view(np.uint32))
+
+    codes, scales = h.dispatch(dev_bf16(xb), mxfp8=True)
+    rc, rs = oracle.dispatch_mxfp8(xb, ref["pos"])
+    assert np.array_equal(host_bits(codes)[:total], rc[:total])
+    assert np.array_equal(host_bits(scales)[:total], rs[:total])
 
     y = make_expert_outputs(T * k, H, seed=2)
     w = rng.uniform(-1, 1, size=(T, k)).astype(np.float32)
@@ -281,9 +286,11 @@ def test_workgroup_cap_gives_identical_results(cap):
     x, idx, w = dev_bf16(wl.x_bits), dev_i32(wl.topk_idx), dev_f32(wl.topk_w)
     y = dev_bf16(make_expert_outputs(s.tokens * s.topk, s.hidden, seed=7))
     h.layout(idx)
-    ref = [h.dispatch(x).view(torch.int16), *h.dispatch(x, fp8=True), h.combine(y, w).view(torch.int16)]
+    ref = [h.dispatch(x).view(torch.int16), *h.dispatch(x, fp8=True), *h.dispatch(x, mxfp8=True),
+           h.combine(y, w).view(torch.int16)]
     h.set_max_workgroups(cap)
-    got = [h.dispatch(x).view(torch.int16), *h.dispatch(x, fp8=True), h.combine(y, w).view(torch.int16)]
+    got = [h.dispatch(x).view(torch.int16), *h.dispatch(x, fp8=True), *h.dispatch(x, mxfp8=True),
+           h.combine(y, w).view(torch.int16)]
     h.set_max_workgroups(0)
     torch.cuda.synchronize()
     for a, b in zip(ref, got):
@@ -308,10 +315,11 @@ def test_bitwise_deterministic_reruns():
         v = {k: t.clone() for k, t in h.view().items()}
         d = h.dispatch(x)
         q, sc = h.dispatch(x, fp8=True)
+        mq, ms = h.dispatch(x, mxfp8=True)
         c = h.combine(y, w)
         torch.cuda.synchronize()
         cur = [v["pos"], v["src_idx"], v["counts_e"], d.view(torch.int16), q, sc.view(torch.int32),
-               c.view(torch.int16)]
+               mq, ms, c.view(torch.int16)]
         if first is None:
             first = cur
         else:
@@ -347,6 +355,8 @@ def test_host_errors_enqueue_nothing():
     h2.layout(dev_i32(np.zeros((4, 2), np.int32)))
     with pytest.raises(MoeError, match="multiple of 128"):
         h2.dispatch(dev_bf16(np.zeros((4, 200), np.uint16)), fp8=True)
+    with pytest.raises(MoeError, match="multiple of 128"):
+        h2.dispatch(dev_bf16(np.zeros((4, 200), np.uint16)), mxfp8=True)
     with pytest.raises(MoeError, match="capacity"):
         h.combine(small, dev_f32(wl.topk_w))
     torch.cuda.synchronize()
