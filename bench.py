@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sustained-iters", type=int, default=30,
                     help="per-op timings, each op back to back over the rotating buffer sets")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1536)
     ap.add_argument("--workgroup-sweep", type=int, default=1,
                     help="1: also report GB/s against a cap on the payload kernels' workgroups")
     ap.add_argument("--buffer-sets", type=int, default=3,
