@@ -38,7 +38,8 @@ import numpy as np
 
 from .codecs import bf16_decode, bf16_encode, e4m3_decode, e4m3_encode
 
-__all__ = ["layout", "dispatch_bf16", "dispatch_fp8", "combine", "dequant_fp8",
+__all__ = ["layout", "layout_fixed_capacity", "dispatch_bf16", "dispatch_fp8", "combine",
+           "dequant_fp8",
            "rank_layout", "dispatch_ranks", "combine_ranks", "quantize_mxfp8_rows",
            "dispatch_mxfp8", "dequant_mxfp8", "e8m0_decode", "FP8_BLOCK", "FP8_MAX", "MX_BLOCK"]
 
@@ -102,6 +103,45 @@ def layout(topk_idx, num_experts: int, num_ranks: int) -> dict:
     }
 
 
+def layout_fixed_capacity(topk_idx, num_experts: int, capacity: int) -> dict:
+    """Placement into fixed per-expert regions (the decode-time layout).
+
+    DeepEP's low-latency kernel family, the decode path of "Inside the Nebius
+    + PyTorch DeepSeek V3 recipe", section "DeepEP", receives into buffers
+    whose shape does not depend on the routing. Reading: expert e owns rows
+    [e*C, (e+1)*C); within it, slots keep the stable (token, slot) order of
+    the standard layout; a slot whose rank within its expert is C or more is
+    dropped (pos = -1, counted). Ids outside [0, E) are skipped as invalid.
+
+    Returns pos int64 [T, k], counts int64 [E] (rows received, at most C),
+    and the ints ``dropped`` and ``invalid``.
+    """
+    idx = np.asarray(topk_idx)
+    T, k = idx.shape
+    E, C = int(num_experts), int(capacity)
+    if E <= 0 or C <= 0:
+        raise ValueError("num_experts and capacity must be positive")
+    rows = idx.tolist()
+    seen = [0] * E                 # slots routed to each expert so far
+    pos = [[-1] * k for _ in range(T)]
+    dropped = invalid = 0
+    for t in range(T):
+        for j in range(k):
+            e = rows[t][j]
+            if not 0 <= e < E:
+                invalid += 1
+                continue
+            r = seen[e]
+            seen[e] = r + 1
+            if r < C:
+                pos[t][j] = e * C + r
+            else:
+                dropped += 1
+    return {"pos": np.asarray(pos, dtype=np.int64).reshape(T, k),
+            "counts": np.minimum(np.asarray(seen, dtype=np.int64), C),
+            "dropped": dropped, "invalid": invalid}
+
+
 def _scatter_rows(rows_per_token: np.ndarray, pos: np.ndarray, capacity: int, fill):
     """out[pos[t, j]] = rows_per_token[t] for every valid slot; other rows = fill."""
     T, k = pos.shape
@@ -113,12 +153,13 @@ def _scatter_rows(rows_per_token: np.ndarray, pos: np.ndarray, capacity: int, fi
     return out
 
 
-def dispatch_bf16(x_bits, pos) -> np.ndarray:
-    """Copy token rows (bf16 bit patterns, uint16 [T, H]) to their T*k rows."""
+def dispatch_bf16(x_bits, pos, rows=None) -> np.ndarray:
+    """Copy token rows (bf16 bit patterns, uint16 [T, H]) to their rows
+    (``rows`` rows in all, T*k by default)."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     pos = np.asarray(pos)
     T, k = pos.shape
-    return _scatter_rows(x_bits, pos, T * k, 0)
+    return _scatter_rows(x_bits, pos, T * k if rows is None else rows, 0)
 
 
 def quantize_fp8_rows(x_bits):
@@ -141,17 +182,18 @@ def quantize_fp8_rows(x_bits):
     return codes, scale
 
 
-def dispatch_fp8(x_bits, pos):
+def dispatch_fp8(x_bits, pos, rows=None):
     """FP8 dispatch: quantise each token once, write codes + scales to its rows.
 
-    Returns (codes uint8 [T*k, H], scales float32 [T*k, H/128]); rows that no
-    slot maps to hold zeros.
+    Returns (codes uint8 [rows, H], scales float32 [rows, H/128]), rows = T*k
+    by default; rows that no slot maps to hold zeros.
     """
     pos = np.asarray(pos)
     T, k = pos.shape
+    n = T * k if rows is None else rows
     codes, scale = quantize_fp8_rows(x_bits)
-    return (_scatter_rows(codes, pos, T * k, 0),
-            _scatter_rows(scale, pos, T * k, np.float32(0.0)))
+    return (_scatter_rows(codes, pos, n, 0),
+            _scatter_rows(scale, pos, n, np.float32(0.0)))
 
 
 def combine(y_bits, w, pos, tokens=None, return_magnitude: bool = False):
@@ -339,12 +381,14 @@ def quantize_mxfp8_rows(x_bits):
     return codes, (shared + 127).astype(np.uint8)
 
 
-def dispatch_mxfp8(x_bits, pos):
-    """MXFP8 dispatch: quantise each token once, write codes + E8M0 scales to its rows."""
+def dispatch_mxfp8(x_bits, pos, rows=None):
+    """MXFP8 dispatch: quantise each token once, write codes + E8M0 scales to its
+    rows (T*k rows by default)."""
     pos = np.asarray(pos)
     T, k = pos.shape
+    n = T * k if rows is None else rows
     codes, scale = quantize_mxfp8_rows(x_bits)
-    return (_scatter_rows(codes, pos, T * k, 0), _scatter_rows(scale, pos, T * k, 0))
+    return (_scatter_rows(codes, pos, n, 0), _scatter_rows(scale, pos, n, 0))
 
 
 def dequant_mxfp8(codes, scales) -> np.ndarray:
