@@ -73,8 +73,7 @@ def cpu_baseline(wl, sample_tokens: int):
     s = wl.shape
     T, H, k = sample_tokens, s.hidden, s.topk
     x = wl.x_bits[:T]
-    idx = wl.topk_idx[:T]
-    w = wl.topk_w[:T]
+    idx, w = oracle.route(wl.logits[:T], k, s.weights)   # the routing is not timed
     t0 = time.perf_counter()
     lay = oracle.layout(idx, s.experts, s.ranks)
     t1 = time.perf_counter()
@@ -127,6 +126,11 @@ def main():
     T, H, k, E, R = s.tokens, s.hidden, s.topk, s.experts, s.ranks
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    h = Handle(T, H, k, E, R, device=dev)
+    # Router outputs from the library's router kernel (untimed set-up).
+    logits = torch.from_numpy(wl.logits).to(dev)
+    topk_idx, topk_w = h.route(logits, s.weights)
+    torch.cuda.synchronize()
 
     # Consecutive steps use different buffer sets (inputs and outputs, about
     # 0.84 GB each), so no step finds the previous step's data in the 256 MB
@@ -136,14 +140,13 @@ def main():
     for _ in range(args.buffer_sets):
         sets.append({
             "x": torch.from_numpy(wl.x_bits.view(np.int16)).view(torch.bfloat16).to(dev),
-            "idx": torch.from_numpy(wl.topk_idx).to(dev),
-            "w": torch.from_numpy(wl.topk_w).to(dev),
+            "idx": topk_idx.clone(),
+            "w": topk_w.clone(),
             "d_out": torch.empty((S, H), dtype=torch.bfloat16, device=dev),
             "q_out": torch.empty((S, H), dtype=torch.uint8, device=dev),
             "q_scales": torch.empty((S, H // 128), dtype=torch.float32, device=dev),
             "c_out": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
         })
-    h = Handle(T, H, k, E, R, device=dev)
     ops = ("layout", "dispatch_bf16", "dispatch_fp8", "combine")
     cur = {"i": 0}
 
@@ -319,6 +322,64 @@ def main():
             sweep["uncapped" if cap == 0 else str(cap)] = row
         h.set_max_workgroups(0)
 
+    def sustained_us(fn, iters):
+        """Median µs of fn(i) over back-to-back calls (3 untimed first)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for i in range(3 + iters):
+            if i >= 3:
+                evs[i - 3][0].record(stream)
+            fn(i)
+            if i >= 3:
+                evs[i - 3][1].record(stream)
+        torch.cuda.synchronize()
+        return round(float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs])), 2)
+
+    # Router at the prefill shape, and the decode-time path at 128 tokens
+    # (fixed per-expert capacity 128: no slot can be dropped).
+    router, decode = {}, {}
+    if args.sustained_iters > 0:
+        rbytes = 4 * T * E + 8 * T * k
+        lg = [logits.clone() for _ in range(len(sets))]
+        us = sustained_us(lambda i: h.route(lg[i % len(lg)], s.weights, topk_idx=sets[0]["idx"],
+                                            topk_w=sets[0]["w"]), args.sustained_iters)
+        router = {"tokens": T, "experts": E, "topk": k, "score": s.weights, "bytes": rbytes,
+                  "us_median": us, "GBps": round(rbytes / (us * 1e-6) / 1e9, 1)}
+        Td, C = 128, 128
+        hd = Handle(Td, H, k, E, R, device=dev)
+        dsets = []
+        for b in sets:
+            di, dw = hd.route(logits[:Td].contiguous(), s.weights)
+            dsets.append({"idx": di, "w": dw, "x": b["x"][:Td].contiguous(),
+                          "lg": logits[:Td].clone(),
+                          "out": torch.empty((E * C, H), dtype=torch.bfloat16, device=dev),
+                          "q": torch.empty((E * C, H), dtype=torch.uint8, device=dev),
+                          "qs": torch.empty((E * C, H // 128), dtype=torch.float32, device=dev),
+                          "std": torch.empty((Td * k, H), dtype=torch.bfloat16, device=dev),
+                          "c": torch.empty((Td, H), dtype=torch.bfloat16, device=dev)})
+        D = lambda i: dsets[i % len(dsets)]   # noqa: E731
+        torch.cuda.synchronize()
+        decode["tokens"], decode["capacity"] = Td, C
+        decode["route_us"] = sustained_us(
+            lambda i: hd.route(D(i)["lg"], s.weights, topk_idx=D(i)["idx"], topk_w=D(i)["w"]),
+            args.sustained_iters)
+        decode["ll_dispatch_bf16_us"] = sustained_us(
+            lambda i: hd.ll_dispatch(D(i)["idx"], D(i)["x"], C, out=D(i)["out"]), args.sustained_iters)
+        decode["ll_dispatch_fp8_us"] = sustained_us(
+            lambda i: hd.ll_dispatch(D(i)["idx"], D(i)["x"], C, "fp8", out=D(i)["q"], scales=D(i)["qs"]),
+            args.sustained_iters)
+        decode["ll_combine_us"] = sustained_us(
+            lambda i: hd.ll_combine(D(i)["out"], D(i)["w"], out=D(i)["c"]), args.sustained_iters)
+
+        def std_path(i):
+            hd.layout(D(i)["idx"])
+            hd.dispatch(D(i)["x"], out=D(i)["std"])
+        decode["layout_plus_dispatch_bf16_us"] = sustained_us(std_path, args.sustained_iters)
+        decode["combine_us"] = sustained_us(
+            lambda i: hd.combine(D(i)["std"], D(i)["w"], out=D(i)["c"]), args.sustained_iters)
+        decode["payload_bytes_bf16"] = 2 * Td * H + 2 * Td * k * H
+        del dsets, hd
+
     dominant = max(("dispatch_bf16", "dispatch_fp8", "combine"), key=lambda n: per_op[n]["us_mean"])
     achieved = per_op[dominant]["GBps"]
     result = {
@@ -346,6 +407,8 @@ def main():
         "sustained": sustained,
         "workgroup_sweep_GBps": sweep,
         "rank_exchange": exchange,
+        "router": router,
+        "decode": decode,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)

@@ -16,15 +16,17 @@ import torch
 
 from . import _lib
 from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP8_E4M3, MOE_MX_BLOCK,
-                   MOE_EP_FP8_BLOCK, MOE_EP_MAX_EXPERTS,
-                   MOE_EP_MAX_TOPK, MOE_EP_STATUS_WORDS, MoeConfig, MoeError, MoeLayoutView,
-                   MoeRankLayoutView)
+                   MOE_EP_FP8_BLOCK, MOE_EP_LL_MAX_TOKENS, MOE_EP_MAX_EXPERTS,
+                   MOE_EP_MAX_TOPK, MOE_EP_STATUS_WORDS, MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX,
+                   MoeConfig, MoeError, MoeLayoutView, MoeLlView, MoeRankLayoutView)
 
 __all__ = ["Handle", "MoeError", "MoeConfig", "moe_workspace_bytes", "moe_handle_create",
            "moe_handle_destroy", "moe_dispatch_layout", "moe_layout_view", "moe_dispatch",
            "moe_combine", "moe_rank_layout", "moe_rank_layout_view", "moe_dispatch_ranks",
-           "moe_combine_ranks", "moe_set_max_workgroups", "moe_status_string", "moe_last_error",
-           "MOE_DTYPE_BF16", "MOE_DTYPE_MXFP8_E4M3",
+           "moe_combine_ranks", "moe_set_max_workgroups", "moe_route", "moe_ll_dispatch",
+           "moe_ll_view", "moe_ll_combine", "moe_status_string", "moe_last_error",
+           "MOE_DTYPE_BF16", "MOE_DTYPE_MXFP8_E4M3", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
+           "MOE_EP_LL_MAX_TOKENS",
            "MOE_DTYPE_FP8_E4M3", "MOE_EP_MAX_EXPERTS", "MOE_EP_MAX_TOPK", "MOE_EP_FP8_BLOCK"]
 
 
@@ -150,6 +152,53 @@ def moe_set_max_workgroups(h: int, max_workgroups: int) -> None:
     _lib.check(_lib.load().moe_set_max_workgroups(ctypes.c_void_p(h), int(max_workgroups)))
 
 
+def moe_route(h: int, logits: torch.Tensor, score: int, topk_idx: torch.Tensor,
+              topk_w: torch.Tensor, stream=None) -> None:
+    pl = _ptr(logits, torch.float32, "logits")
+    pi = _ptr(topk_idx, torch.int32, "topk_idx")
+    pw = _ptr(topk_w, torch.float32, "topk_w")
+    _lib.check(_lib.load().moe_route(ctypes.c_void_p(h), ctypes.c_void_p(pl), int(logits.shape[0]),
+                                     int(score), ctypes.c_void_p(pi), ctypes.c_void_p(pw),
+                                     _stream(stream, logits.device)))
+
+
+def _payload_ptrs(x, dtype, out, scales):
+    px = _ptr(x, torch.bfloat16, "x")
+    po = _ptr(out, torch.bfloat16 if dtype == MOE_DTYPE_BF16 else torch.uint8, "out")
+    ps = None
+    if dtype == MOE_DTYPE_FP8_E4M3:
+        ps = _ptr(scales, torch.float32, "scales")
+    elif dtype == MOE_DTYPE_MXFP8_E4M3:
+        ps = _ptr(scales, torch.uint8, "scales")
+    return px, po, ps
+
+
+def moe_ll_dispatch(h: int, topk_idx: torch.Tensor, capacity: int, x: torch.Tensor, dtype: int,
+                    out: torch.Tensor, scales: torch.Tensor | None, stream=None) -> None:
+    pi = _ptr(topk_idx, torch.int32, "topk_idx")
+    px, po, ps = _payload_ptrs(x, dtype, out, scales)
+    _lib.check(_lib.load().moe_ll_dispatch(
+        ctypes.c_void_p(h), ctypes.c_void_p(pi), int(topk_idx.shape[0]), int(capacity),
+        ctypes.c_void_p(px), int(dtype), ctypes.c_void_p(po), ctypes.c_void_p(ps), out.shape[0],
+        _stream(stream, x.device)))
+
+
+def moe_ll_view(h: int) -> MoeLlView:
+    v = MoeLlView()
+    _lib.check(_lib.load().moe_ll_view(ctypes.c_void_p(h), ctypes.byref(v)))
+    return v
+
+
+def moe_ll_combine(h: int, y: torch.Tensor, w: torch.Tensor, out: torch.Tensor,
+                   stream=None) -> None:
+    py = _ptr(y, torch.bfloat16, "y")
+    pw = _ptr(w, torch.float32, "w")
+    po = _ptr(out, torch.bfloat16, "out")
+    _lib.check(_lib.load().moe_ll_combine(ctypes.c_void_p(h), ctypes.c_void_p(py), y.shape[0],
+                                          ctypes.c_void_p(pw), ctypes.c_void_p(po),
+                                          _stream(stream, y.device)))
+
+
 def moe_status_string(status: int) -> str:
     return _lib.load().moe_status_string(int(status)).decode()
 
@@ -175,6 +224,7 @@ class Handle:
         self._destroy = _lib.load().moe_handle_destroy   # kept for use at interpreter exit
         self.num_tokens = None
         self.rank_num_tokens = None
+        self.ll_num_tokens = None
 
     def __del__(self):
         h = getattr(self, "h", None)
@@ -230,6 +280,65 @@ class Handle:
                 "slot_row": arr(v.slot_row, T * self.topk).view(T, self.topk),
                 "rank_src": arr(v.src_idx, cap), "counts_r": arr(v.counts_r, R),
                 "offsets_r": arr(v.offsets_r, R + 1), "status": arr(v.status, MOE_EP_STATUS_WORDS)}
+
+    # ---- router
+    def route(self, logits: torch.Tensor, score: str = "softmax", topk_idx=None, topk_w=None,
+              stream=None):
+        """fp32 logits [T, E] -> (topk_idx int32 [T, k], topk_w fp32 [T, k])."""
+        _ptr(logits, torch.float32, "logits", self.device)
+        code = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}[score]
+        T = int(logits.shape[0])
+        if topk_idx is None:
+            topk_idx = torch.empty((T, self.topk), dtype=torch.int32, device=self.device)
+        if topk_w is None:
+            topk_w = torch.empty((T, self.topk), dtype=torch.float32, device=self.device)
+        moe_route(self.h, logits, code, topk_idx, topk_w, stream)
+        return topk_idx, topk_w
+
+    # ---- decode-time (fixed-capacity) dispatch and combine
+    def ll_dispatch(self, topk_idx: torch.Tensor, x: torch.Tensor, capacity: int,
+                    dtype: str = "bf16", out=None, scales=None, stream=None):
+        """Rows [E * capacity, H]: bf16, or (codes, scales) for "fp8" / "mxfp8"."""
+        _ptr(topk_idx, torch.int32, "topk_idx", self.device)
+        _ptr(x, torch.bfloat16, "x", self.device)
+        code = {"bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_E4M3,
+                "mxfp8": MOE_DTYPE_MXFP8_E4M3}[dtype]
+        rows = self.num_experts * int(capacity)
+        if out is None:
+            out = torch.empty((rows, self.hidden),
+                              dtype=torch.bfloat16 if code == MOE_DTYPE_BF16 else torch.uint8,
+                              device=self.device)
+        if scales is None and code == MOE_DTYPE_FP8_E4M3:
+            scales = torch.empty((rows, self.hidden // MOE_EP_FP8_BLOCK), dtype=torch.float32,
+                                 device=self.device)
+        if scales is None and code == MOE_DTYPE_MXFP8_E4M3:
+            scales = torch.empty((rows, self.hidden // MOE_MX_BLOCK), dtype=torch.uint8,
+                                 device=self.device)
+        moe_ll_dispatch(self.h, topk_idx, capacity, x, code, out, scales, stream)
+        self.ll_num_tokens = int(topk_idx.shape[0])
+        return out if code == MOE_DTYPE_BF16 else (out, scales)
+
+    def ll_view(self) -> dict:
+        """Positions [T, k], counts [E] and status [4] of the last ll_dispatch."""
+        v = moe_ll_view(self.h)
+        base = self.workspace.data_ptr()
+
+        def arr(ptr, n):
+            off = ptr - base
+            return self.workspace[off:off + 4 * n].view(torch.int32)
+
+        T = v.num_tokens
+        return {"pos": arr(v.pos, T * self.topk).view(T, self.topk),
+                "counts": arr(v.counts, self.num_experts), "status": arr(v.status, 4),
+                "capacity": v.capacity, "rows": v.rows}
+
+    def ll_combine(self, y: torch.Tensor, w: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+        _ptr(y, torch.bfloat16, "y", self.device)
+        if out is None:
+            out = torch.empty((self.ll_num_tokens, self.hidden), dtype=torch.bfloat16,
+                              device=self.device)
+        moe_ll_combine(self.h, y, w, out, stream)
+        return out
 
     def set_max_workgroups(self, n: int) -> None:
         """Cap dispatch/combine at n workgroups (0: no cap)."""

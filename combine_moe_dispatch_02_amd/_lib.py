@@ -19,12 +19,16 @@ MOE_EP_MAX_EXPERTS = 1024
 MOE_EP_MAX_TOPK = 32
 MOE_EP_FP8_BLOCK = 128
 MOE_EP_STATUS_WORDS = 4
+MOE_EP_LL_MAX_TOKENS = 1024
+MOE_SCORE_SOFTMAX = 0
+MOE_SCORE_SIGMOID = 1
 
 # Every function the header declares, for the export check.
 EXPORTS = ("moe_workspace_bytes", "moe_handle_create", "moe_handle_destroy",
            "moe_dispatch_layout", "moe_layout_view", "moe_dispatch", "moe_combine",
            "moe_rank_layout", "moe_rank_layout_view", "moe_dispatch_ranks", "moe_combine_ranks",
-           "moe_set_max_workgroups", "moe_status_string", "moe_last_error")
+           "moe_set_max_workgroups", "moe_route", "moe_ll_dispatch", "moe_ll_view",
+           "moe_ll_combine", "moe_status_string", "moe_last_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -46,6 +50,12 @@ class MoeRankLayoutView(ctypes.Structure):
                 ("src_idx", ctypes.c_void_p), ("counts_r", ctypes.c_void_p),
                 ("offsets_r", ctypes.c_void_p), ("status", ctypes.c_void_p),
                 ("num_tokens", ctypes.c_int32), ("capacity", ctypes.c_int64)]
+
+
+class MoeLlView(ctypes.Structure):
+    _fields_ = [("pos", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+                ("status", ctypes.c_void_p), ("num_tokens", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("rows", ctypes.c_int64)]
 
 
 class MoeError(RuntimeError):
@@ -87,6 +97,10 @@ def load() -> ctypes.CDLL:
         "moe_dispatch_ranks": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i64, vp]),
         "moe_combine_ranks": (ctypes.c_int, [vp, vp, i64, vp, vp]),
         "moe_set_max_workgroups": (ctypes.c_int, [vp, i32]),
+        "moe_route": (ctypes.c_int, [vp, vp, i32, ctypes.c_int, vp, vp, vp]),
+        "moe_ll_dispatch": (ctypes.c_int, [vp, vp, i32, i32, vp, ctypes.c_int, vp, vp, i64, vp]),
+        "moe_ll_view": (ctypes.c_int, [vp, ctypes.POINTER(MoeLlView)]),
+        "moe_ll_combine": (ctypes.c_int, [vp, vp, i64, vp, vp, vp]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
     }

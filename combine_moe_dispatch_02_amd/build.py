@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoe_ep.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.cpp", "layout.hip", "dispatch.hip", "combine.hip"]
+SOURCES = ["api.cpp", "layout.hip", "dispatch.hip", "combine.hip", "router.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

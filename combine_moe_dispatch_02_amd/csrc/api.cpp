@@ -1,6 +1,6 @@
 // C ABI of the dispatch/combine library: argument checks, workspace carving,
-// handle state and error reporting. Kernels live in layout.hip, dispatch.hip
-// and combine.hip.
+// handle state and error reporting. Kernels live in layout.hip, dispatch.hip,
+// combine.hip and router.hip.
 //
 // Conventions (declared in moe_ep.h): nothing throws across the ABI, host-side
 // argument errors enqueue nothing, device work is asynchronous on the caller's
@@ -27,6 +27,13 @@ struct moe_handle {
   bool rank_ready;
   int32_t rank_num_tokens;
   int32_t max_workgroups;  // 0: one workgroup per 4 work items
+  // Decode-time (fixed-capacity) state.
+  int32_t* ll_pos;     // [min(T_max, LL max) * k]
+  int32_t* ll_counts;  // [E]
+  int32_t* ll_status;  // [MOE_EP_STATUS_WORDS]
+  bool ll_ready;
+  int32_t ll_num_tokens;
+  int32_t ll_capacity;
 };
 
 namespace {
@@ -58,6 +65,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Carve {
   size_t status, counts_e, offsets_e, counts_r, offsets_r, hist, pos, src_idx;
   size_t r_status, r_counts, r_offsets, r_hist, r_slot_row, r_rank_pos, r_src;
+  size_t ll_pos, ll_counts, ll_status;
   size_t total;
 };
 
@@ -86,6 +94,10 @@ Carve carve(const moe_config_t& c) {
   r.r_slot_row = take(sizeof(int32_t) * size_t(slots));
   r.r_rank_pos = take(sizeof(int32_t) * size_t(c.max_tokens) * c.num_ranks);
   r.r_src = take(sizeof(int32_t) * size_t(rank_rows));
+  const int64_t ll_tokens = c.max_tokens < MOE_EP_LL_MAX_TOKENS ? c.max_tokens : MOE_EP_LL_MAX_TOKENS;
+  r.ll_pos = take(sizeof(int32_t) * size_t(ll_tokens) * c.topk);
+  r.ll_counts = take(sizeof(int32_t) * c.num_experts);
+  r.ll_status = take(sizeof(int32_t) * MOE_EP_STATUS_WORDS);
   r.total = off;
   return r;
 }
@@ -207,6 +219,12 @@ int moe_handle_create(const moe_config_t* cfg, void* d_workspace, size_t ws_byte
   h->rank_ready = false;
   h->rank_num_tokens = 0;
   h->max_workgroups = 0;
+  h->ll_pos = at(c.ll_pos);
+  h->ll_counts = at(c.ll_counts);
+  h->ll_status = at(c.ll_status);
+  h->ll_ready = false;
+  h->ll_num_tokens = 0;
+  h->ll_capacity = 0;
   *out = h;
   return ok();
 }
@@ -270,24 +288,13 @@ int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, void* 
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: x or out is NULL");
   if (!aligned(d_x, 16) || !aligned(d_out, 16))
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: x and out must be 16-byte aligned");
-  hipError_t err;
-  if (dtype == MOE_DTYPE_BF16) {
-    err = moe::launch_dispatch_bf16(d_x, h->arrays.pos, d_out, out_rows, h->num_tokens,
-                                    h->cfg.topk, h->cfg.hidden, h->max_workgroups, stream);
-  } else {
-    if (d_scales == nullptr)
-      return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: FP8 dispatch needs a scales buffer");
-    if (!aligned(d_scales, 4))
-      return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: scales must be 4-byte aligned");
-    if (dtype == MOE_DTYPE_FP8_E4M3)
-      err = moe::launch_dispatch_fp8(d_x, h->arrays.pos, d_out, static_cast<float*>(d_scales),
-                                     out_rows, h->num_tokens, h->cfg.topk, h->cfg.hidden,
-                                     h->max_workgroups, stream);
-    else
-      err = moe::launch_dispatch_mxfp8(d_x, h->arrays.pos, d_out, d_scales, out_rows,
-                                       h->num_tokens, h->cfg.topk, h->cfg.hidden,
-                                       h->max_workgroups, stream);
-  }
+  if (dtype != MOE_DTYPE_BF16 && d_scales == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: FP8 dispatch needs a scales buffer");
+  if (dtype != MOE_DTYPE_BF16 && !aligned(d_scales, 4))
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: scales must be 4-byte aligned");
+  const hipError_t err =
+      moe::launch_dispatch(dtype, d_x, h->arrays.pos, d_out, d_scales, out_rows, h->num_tokens,
+                           h->cfg.topk, h->cfg.hidden, h->max_workgroups, stream);
   return hip_status(err, "moe_dispatch");
 }
 
@@ -367,9 +374,9 @@ int moe_dispatch_ranks(moe_handle_t h, const void* d_x, const int32_t* d_topk_id
       !aligned(d_recv_idx, 4) || !aligned(d_recv_w, 4))
     return fail(MOE_ERR_INVALID_ARG,
                 "moe_dispatch_ranks: x and out must be 16-byte aligned, the rest 4-byte aligned");
-  hipError_t err = moe::launch_dispatch_bf16(d_x, h->rank.slot_row, d_out, out_rows,
-                                             h->rank_num_tokens, h->cfg.topk, h->cfg.hidden,
-                                             h->max_workgroups, stream);
+  hipError_t err = moe::launch_dispatch(MOE_DTYPE_BF16, d_x, h->rank.slot_row, d_out, nullptr,
+                                        out_rows, h->rank_num_tokens, h->cfg.topk, h->cfg.hidden,
+                                        h->max_workgroups, stream);
   if (err == hipSuccess)
     err = moe::launch_rank_meta(d_topk_idx, d_w, h->rank.slot_row, h->rank_num_tokens,
                                 h->cfg.topk, h->cfg.num_experts, h->cfg.num_ranks, out_rows,
@@ -404,6 +411,105 @@ int moe_set_max_workgroups(moe_handle_t h, int32_t max_workgroups) {
                 max_workgroups);
   h->max_workgroups = max_workgroups;
   return ok();
+}
+
+int moe_route(moe_handle_t h, const float* d_logits, int32_t num_tokens, int score,
+              int32_t* d_topk_idx, float* d_topk_w, hipStream_t stream) {
+  if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_route: handle is NULL");
+  if (num_tokens < 0 || num_tokens > h->cfg.max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: num_tokens=%d outside [0, %d]", num_tokens,
+                h->cfg.max_tokens);
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: unknown score %d", score);
+  if (num_tokens == 0) return ok();
+  if (d_logits == nullptr || d_topk_idx == nullptr || d_topk_w == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: logits, topk_idx or topk_w is NULL");
+  if (!aligned(d_logits, 4) || !aligned(d_topk_idx, 4) || !aligned(d_topk_w, 4))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: pointers must be 4-byte aligned");
+  const hipError_t err = moe::launch_route(d_logits, num_tokens, h->cfg.num_experts, h->cfg.topk,
+                                           score, d_topk_idx, d_topk_w, stream);
+  return hip_status(err, "moe_route");
+}
+
+int moe_ll_dispatch(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_tokens,
+                    int32_t capacity, const void* d_x, int dtype, void* d_out, void* d_scales,
+                    int64_t out_rows, hipStream_t stream) {
+  if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_ll_dispatch: handle is NULL");
+  const int32_t limit =
+      h->cfg.max_tokens < MOE_EP_LL_MAX_TOKENS ? h->cfg.max_tokens : MOE_EP_LL_MAX_TOKENS;
+  if (num_tokens < 0 || num_tokens > limit)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_ll_dispatch: num_tokens=%d outside [0, %d] (min of max_tokens and "
+                "MOE_EP_LL_MAX_TOKENS; use moe_dispatch_layout + moe_dispatch for large batches)",
+                num_tokens, limit);
+  if (capacity < 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_ll_dispatch: capacity=%d must be >= 1", capacity);
+  const int64_t rows = int64_t(h->cfg.num_experts) * capacity;
+  if (rows > kMaxSlots)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_ll_dispatch: num_experts*capacity=%lld exceeds %lld rows",
+                (long long)rows, (long long)kMaxSlots);
+  if (out_rows < rows)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_ll_dispatch: out_rows=%lld is below num_experts*capacity=%lld",
+                (long long)out_rows, (long long)rows);
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3 && dtype != MOE_DTYPE_MXFP8_E4M3)
+    return fail(MOE_ERR_INVALID_ARG, "moe_ll_dispatch: unknown dtype %d", dtype);
+  if (dtype != MOE_DTYPE_BF16 && h->cfg.hidden % MOE_EP_FP8_BLOCK != 0)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_ll_dispatch: FP8 and MXFP8 need hidden to be a multiple of %d; hidden=%d",
+                MOE_EP_FP8_BLOCK, h->cfg.hidden);
+  if (num_tokens > 0 && (d_topk_idx == nullptr || d_x == nullptr || d_out == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "moe_ll_dispatch: topk_idx, x or out is NULL");
+  if (num_tokens > 0 && dtype != MOE_DTYPE_BF16 && d_scales == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_ll_dispatch: FP8 dispatch needs a scales buffer");
+  if (!aligned(d_topk_idx, 4) || !aligned(d_x, 16) || !aligned(d_out, 16) || !aligned(d_scales, 4))
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_ll_dispatch: x and out must be 16-byte aligned, topk_idx and scales 4-byte");
+  const hipError_t err = moe::launch_dispatch_fixed(
+      dtype, d_x, d_topk_idx, num_tokens, h->cfg.topk, h->cfg.num_experts, capacity, h->ll_pos,
+      h->ll_counts, h->ll_status, d_out, d_scales, h->cfg.hidden, h->max_workgroups, stream);
+  if (err != hipSuccess) {
+    h->ll_ready = false;
+    return hip_status(err, "moe_ll_dispatch");
+  }
+  h->ll_ready = true;
+  h->ll_num_tokens = num_tokens;
+  h->ll_capacity = capacity;
+  return ok();
+}
+
+int moe_ll_view(moe_handle_t h, moe_ll_view_t* out) {
+  if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_ll_view: out is NULL");
+  if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_ll_view: handle is NULL");
+  if (!h->ll_ready)
+    return fail(MOE_ERR_STATE, "moe_ll_view: no decode-time dispatch yet; call moe_ll_dispatch");
+  out->pos = h->ll_pos;
+  out->counts = h->ll_counts;
+  out->status = h->ll_status;
+  out->num_tokens = h->ll_num_tokens;
+  out->capacity = h->ll_capacity;
+  out->rows = int64_t(h->cfg.num_experts) * h->ll_capacity;
+  return ok();
+}
+
+int moe_ll_combine(moe_handle_t h, const void* d_y, int64_t y_rows, const float* d_w,
+                   void* d_out, hipStream_t stream) {
+  if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_ll_combine: handle is NULL");
+  if (!h->ll_ready)
+    return fail(MOE_ERR_STATE, "moe_ll_combine: no decode-time dispatch yet; call moe_ll_dispatch");
+  const int64_t rows = int64_t(h->cfg.num_experts) * h->ll_capacity;
+  if (y_rows < rows)
+    return fail(MOE_ERR_INVALID_ARG, "moe_ll_combine: y_rows=%lld is below num_experts*capacity=%lld",
+                (long long)y_rows, (long long)rows);
+  if (h->ll_num_tokens == 0) return ok();
+  if (d_y == nullptr || d_w == nullptr || d_out == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_ll_combine: y, w or out is NULL");
+  if (!aligned(d_y, 16) || !aligned(d_out, 16) || !aligned(d_w, 4))
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_ll_combine: y and out must be 16-byte aligned, w 4-byte aligned");
+  const hipError_t err = moe::launch_combine(d_y, y_rows, d_w, h->ll_pos, d_out, h->ll_num_tokens,
+                                             h->cfg.topk, h->cfg.hidden, h->max_workgroups, stream);
+  return hip_status(err, "moe_ll_combine");
 }
 
 const char* moe_status_string(int status) {

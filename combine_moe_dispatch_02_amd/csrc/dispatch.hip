@@ -31,6 +31,19 @@
 // rounds to 448 anyway, and the clamp keeps the conversion away from its
 // overflow handling. A block whose amax is 0 gets scale 0 and its
 // signed-zero inputs as codes.
+//
+// Decode-time (fixed-capacity) dispatch does layout and payload in one launch.
+// DeepEP's second kernel family serves decode ("Inside the Nebius + PyTorch
+// DeepSeek V3 recipe", section "DeepEP"); its receive buffers have a shape
+// that does not depend on the routing. Here expert e owns rows
+// [e*C, (e+1)*C); a slot's row is e*C plus its stable rank among the slots
+// routed to e (token order, then slot order), and slots ranked C or more are
+// dropped. Each wavefront computes the ranks of its own token's slots by
+// counting matching ids among all earlier slots (one coalesced load and one
+// ballot per 64 slots and slot), so no workgroup waits for another; the last
+// workgroup of the grid builds the per-expert histogram in LDS and publishes
+// counts and status. The counting costs O(T*k) per wavefront, which is why
+// this path is limited to small batches (MOE_EP_LL_MAX_TOKENS).
 #include "moe_internal.h"
 
 namespace moe {
@@ -56,22 +69,122 @@ __device__ __forceinline__ void load_rows(const int32_t* __restrict__ pt, int j0
     if (j0 + jj >= topk || p[jj] < 0 || p[jj] >= rows) p[jj] = -1;
 }
 
+// Where a payload kernel finds the destination rows of token t's slots.
+// rows_of fills p[] for slots j0 .. j0+kSlotBatch-1 (-1: no row); `record`
+// is true for exactly one wavefront per token (its first column slice).
+
+// Standard layout: the table pos[T, k] written by the layout kernels.
+struct TableRows {
+  static constexpr bool kCountsBlock = false;
+  const int32_t* pos;
+  int topk;
+  int64_t rows;
+  __device__ __forceinline__ void rows_of(int t, int j0, bool, int (&p)[kSlotBatch]) const {
+    load_rows(pos + static_cast<size_t>(t) * topk, j0, topk, rows, p);
+  }
+  __device__ void counts_block(int) const {}
+};
+
+// Fixed-capacity layout, computed on the fly (decode-time dispatch).
+struct FixedCapacityRows {
+  static constexpr bool kCountsBlock = true;
+  const int32_t* idx;   // [T, k] expert ids
+  int topk, num_experts, capacity;
+  int32_t* pos;         // [T, k] rows, recorded for combine
+  int32_t* counts;      // [E] rows received per expert
+  int32_t* status;      // [4] invalid, placed, T, dropped
+
+  __device__ __forceinline__ void rows_of(int t, int j0, bool record, int (&p)[kSlotBatch]) const {
+    const int base = t * topk;
+    int e[kSlotBatch], rank[kSlotBatch];
+#pragma unroll
+    for (int jj = 0; jj < kSlotBatch; ++jj) {
+      e[jj] = idx[base + (j0 + jj < topk ? j0 + jj : topk - 1)];
+      rank[jj] = 0;
+    }
+    // Rank of slot s = number of earlier slots with the same id.
+    const int lane = threadIdx.x & 63;
+    const int last = base + (j0 + kSlotBatch < topk ? j0 + kSlotBatch : topk);
+    for (int c = 0; c < last; c += 64) {
+      const int s = c + lane;
+      const int id = s < last ? idx[s] : -1;
+#pragma unroll
+      for (int jj = 0; jj < kSlotBatch; ++jj)
+        rank[jj] += __popcll(__ballot(id == e[jj] && s < base + j0 + jj));
+    }
+    int mine = -1;
+#pragma unroll
+    for (int jj = 0; jj < kSlotBatch; ++jj) {
+      const bool ok = j0 + jj < topk && static_cast<unsigned>(e[jj]) <
+                      static_cast<unsigned>(num_experts) && rank[jj] < capacity;
+      p[jj] = ok ? e[jj] * capacity + rank[jj] : -1;
+      if (lane == jj) mine = p[jj];
+    }
+    if (record && lane < kSlotBatch && j0 + lane < topk) pos[base + j0 + lane] = mine;
+  }
+
+  // Run by the grid's last workgroup: histogram of all slots in LDS, then
+  // per-expert counts (clamped to the capacity) and the status words.
+  __device__ void counts_block(int num_tokens) const {
+    __shared__ int hist[MOE_EP_MAX_EXPERTS];
+    __shared__ int tally[2];   // invalid slots, dropped slots
+    const int tid = threadIdx.x, nthreads = blockDim.x;
+    for (int e = tid; e < num_experts; e += nthreads) hist[e] = 0;
+    if (tid < 2) tally[tid] = 0;
+    __syncthreads();
+    const int slots = num_tokens * topk;
+    int bad = 0;
+    for (int s = tid; s < slots; s += nthreads) {
+      const int id = idx[s];
+      if (static_cast<unsigned>(id) < static_cast<unsigned>(num_experts)) atomicAdd(&hist[id], 1);
+      else ++bad;
+    }
+    if (bad) atomicAdd(&tally[0], bad);
+    __syncthreads();
+    int drop = 0;
+    for (int e = tid; e < num_experts; e += nthreads) {
+      const int c = hist[e];
+      counts[e] = c < capacity ? c : capacity;
+      drop += c > capacity ? c - capacity : 0;
+    }
+    if (drop) atomicAdd(&tally[1], drop);
+    __syncthreads();
+    if (tid == 0) {
+      status[0] = tally[0];
+      status[1] = slots - tally[0] - tally[1];
+      status[2] = num_tokens;
+      status[3] = tally[1];
+    }
+  }
+};
+
+// Payload kernels. Workgroups [0, payload_blocks) run the (token, slice)
+// items; with a FixedCapacityRows source one more workgroup follows and
+// publishes the counts.
+template <class Rows>
 __global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_kernel(
-    const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ out,
-    int num_tokens, int topk, int nvec, int slices, int64_t rows) {
+    const u32x4* __restrict__ x, Rows src_rows, u32x4* __restrict__ out, int num_tokens,
+    int nvec, int slices, int payload_blocks) {
+  if constexpr (Rows::kCountsBlock) {
+    if (static_cast<int>(blockIdx.x) == payload_blocks) {
+      src_rows.counts_block(num_tokens);
+      return;
+    }
+  }
   const int lane = threadIdx.x & 63;
   const int nitems = num_tokens * slices;
+  const int topk = src_rows.topk;
   for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
-       item += gridDim.x * kItemWaves) {
+       item += payload_blocks * kItemWaves) {
     const int t = item / slices;
-    const int v = (item - t * slices) * 64 + lane;
+    const int slice = item - t * slices;
+    const int v = slice * 64 + lane;
     const bool active = v < nvec;
     u32x4 r = {0u, 0u, 0u, 0u};
     if (active) r = x[static_cast<size_t>(t) * nvec + v];
-    const int32_t* pt = pos + static_cast<size_t>(t) * topk;
     for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
       int p[kSlotBatch];
-      load_rows(pt, j0, topk, rows, p);
+      src_rows.rows_of(t, j0, slice == 0, p);
 #pragma unroll
       for (int jj = 0; jj < kSlotBatch; ++jj)
         if (p[jj] >= 0 && active) out[static_cast<size_t>(p[jj]) * nvec + v] = r;
@@ -89,17 +202,26 @@ __device__ __forceinline__ uint32_t pack_e4m3(float a, float b, float c, float d
   return static_cast<uint32_t>(w);
 }
 
+template <class Rows>
 __global__ __launch_bounds__(64 * kItemWaves) void dispatch_fp8_kernel(
-    const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ out,
-    float* __restrict__ scales, int num_tokens, int topk, int hidden, int slices, int64_t rows) {
+    const u32x4* __restrict__ x, Rows src_rows, u32x4* __restrict__ out,
+    float* __restrict__ scales, int num_tokens, int hidden, int slices, int payload_blocks) {
+  if constexpr (Rows::kCountsBlock) {
+    if (static_cast<int>(blockIdx.x) == payload_blocks) {
+      src_rows.counts_block(num_tokens);
+      return;
+    }
+  }
   const int lane = threadIdx.x & 63;
   const int units = hidden >> 4;    // 16 channels per lane
   const int nscale = hidden >> 7;   // one scale per 128 channels
   const int nitems = num_tokens * slices;
+  const int topk = src_rows.topk;
   for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
-       item += gridDim.x * kItemWaves) {
+       item += payload_blocks * kItemWaves) {
     const int t = item / slices;
-    const int u = (item - t * slices) * 64 + lane;
+    const int slice = item - t * slices;
+    const int u = slice * 64 + lane;
     // units is a multiple of 8, so each 8-lane group is wholly active or not.
     const bool active = u < units;
     const u32x4* src = x + static_cast<size_t>(t) * (hidden >> 3);
@@ -129,10 +251,9 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_fp8_kernel(
     q.z = pack_e4m3(f[8], f[9], f[10], f[11]);
     q.w = pack_e4m3(f[12], f[13], f[14], f[15]);
     const bool scale_lane = active && (lane & 7) == 0;
-    const int32_t* pt = pos + static_cast<size_t>(t) * topk;
     for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
       int p[kSlotBatch];
-      load_rows(pt, j0, topk, rows, p);
+      src_rows.rows_of(t, j0, slice == 0, p);
 #pragma unroll
       for (int jj = 0; jj < kSlotBatch; ++jj) {
         if (p[jj] < 0) continue;
@@ -153,17 +274,26 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_fp8_kernel(
 // gets code 0 and signed-zero elements. Four E8M0 bytes go out per dword
 // store. The Hybrid-EP news item ("Efficiency Numbers") reports its Qwen3 run
 // in MXFP8.
+template <class Rows>
 __global__ __launch_bounds__(64 * kItemWaves) void dispatch_mxfp8_kernel(
-    const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ out,
-    uint32_t* __restrict__ scales, int num_tokens, int topk, int hidden, int slices, int64_t rows) {
+    const u32x4* __restrict__ x, Rows src_rows, u32x4* __restrict__ out,
+    uint32_t* __restrict__ scales, int num_tokens, int hidden, int slices, int payload_blocks) {
+  if constexpr (Rows::kCountsBlock) {
+    if (static_cast<int>(blockIdx.x) == payload_blocks) {
+      src_rows.counts_block(num_tokens);
+      return;
+    }
+  }
   const int lane = threadIdx.x & 63;
   const int units = hidden >> 4;           // 16 channels per lane
   const int scale_words = hidden >> 7;     // 4 one-byte scales per dword, per row
   const int nitems = num_tokens * slices;
+  const int topk = src_rows.topk;
   for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
-       item += gridDim.x * kItemWaves) {
+       item += payload_blocks * kItemWaves) {
     const int t = item / slices;
-    const int u = (item - t * slices) * 64 + lane;
+    const int slice = item - t * slices;
+    const int u = slice * 64 + lane;
     // units is a multiple of 8, so each 8-lane group is wholly active or not.
     const bool active = u < units;
     const u32x4* src = x + static_cast<size_t>(t) * (hidden >> 3);
@@ -202,10 +332,9 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_mxfp8_kernel(
     const uint32_t c3 = __shfl(code, lane + 6, 64);
     const uint32_t word = code | (c1 << 8) | (c2 << 16) | (c3 << 24);
     const bool scale_lane = active && (lane & 7) == 0;
-    const int32_t* pt = pos + static_cast<size_t>(t) * topk;
     for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
       int p[kSlotBatch];
-      load_rows(pt, j0, topk, rows, p);
+      src_rows.rows_of(t, j0, slice == 0, p);
 #pragma unroll
       for (int jj = 0; jj < kSlotBatch; ++jj) {
         if (p[jj] < 0) continue;
@@ -243,19 +372,6 @@ __global__ __launch_bounds__(256) void rank_meta_kernel(
 
 }  // namespace
 
-hipError_t launch_dispatch_mxfp8(const void* d_x, const int32_t* d_pos, void* d_out,
-                                 void* d_scales, int64_t rows, int num_tokens, int topk,
-                                 int hidden, int max_blocks, hipStream_t stream) {
-  if (num_tokens == 0) return hipSuccess;
-  const int units = hidden / 16;
-  const int slices = (units + 63) / 64;
-  hipLaunchKernelGGL(dispatch_mxfp8_kernel, item_grid(int64_t(num_tokens) * slices, max_blocks),
-                     dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_x), d_pos,
-                     static_cast<u32x4*>(d_out), static_cast<uint32_t*>(d_scales), num_tokens,
-                     topk, hidden, slices, rows);
-  return hipGetLastError();
-}
-
 hipError_t launch_rank_meta(const int32_t* d_idx, const float* d_w, const int32_t* d_slot_row,
                             int num_tokens, int topk, int num_experts, int num_ranks, int64_t rows,
                             int32_t* d_recv_idx, float* d_recv_w, hipStream_t stream) {
@@ -267,28 +383,47 @@ hipError_t launch_rank_meta(const int32_t* d_idx, const float* d_w, const int32_
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_bf16(const void* d_x, const int32_t* d_pos, void* d_out,
-                                int64_t rows, int num_tokens, int topk, int hidden,
-                                int max_blocks, hipStream_t stream) {
-  if (num_tokens == 0) return hipSuccess;
-  const int nvec = hidden / 8;
-  const int slices = (nvec + 63) / 64;
-  hipLaunchKernelGGL(dispatch_bf16_kernel, item_grid(int64_t(num_tokens) * slices, max_blocks),
-                     dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_x), d_pos,
-                     static_cast<u32x4*>(d_out), num_tokens, topk, nvec, slices, rows);
+// Grid of a payload kernel: work-item workgroups (capped by max_blocks),
+// plus the counts workgroup for the fixed-capacity layout.
+template <class Rows>
+hipError_t launch_payload(int dtype, const void* d_x, const Rows& src_rows, void* d_out,
+                          void* d_scales, int num_tokens, int hidden, int max_blocks,
+                          hipStream_t stream) {
+  const int per_lane = dtype == MOE_DTYPE_BF16 ? 8 : 16;   // channels per lane
+  const int slices = (hidden / per_lane + 63) / 64;
+  const int payload = num_tokens == 0 ? 0
+                      : static_cast<int>(item_grid(int64_t(num_tokens) * slices, max_blocks).x);
+  const int blocks = payload + (Rows::kCountsBlock ? 1 : 0);
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid(blocks), block(64 * kItemWaves);
+  const u32x4* x = static_cast<const u32x4*>(d_x);
+  u32x4* out = static_cast<u32x4*>(d_out);
+  if (dtype == MOE_DTYPE_BF16)
+    hipLaunchKernelGGL(dispatch_bf16_kernel<Rows>, grid, block, 0, stream, x, src_rows, out,
+                       num_tokens, hidden / 8, slices, payload);
+  else if (dtype == MOE_DTYPE_FP8_E4M3)
+    hipLaunchKernelGGL(dispatch_fp8_kernel<Rows>, grid, block, 0, stream, x, src_rows, out,
+                       static_cast<float*>(d_scales), num_tokens, hidden, slices, payload);
+  else
+    hipLaunchKernelGGL(dispatch_mxfp8_kernel<Rows>, grid, block, 0, stream, x, src_rows, out,
+                       static_cast<uint32_t*>(d_scales), num_tokens, hidden, slices, payload);
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_fp8(const void* d_x, const int32_t* d_pos, void* d_out,
-                               float* d_scales, int64_t rows, int num_tokens, int topk,
-                               int hidden, int max_blocks, hipStream_t stream) {
-  if (num_tokens == 0) return hipSuccess;
-  const int units = hidden / 16;
-  const int slices = (units + 63) / 64;
-  hipLaunchKernelGGL(dispatch_fp8_kernel, item_grid(int64_t(num_tokens) * slices, max_blocks),
-                     dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_x), d_pos,
-                     static_cast<u32x4*>(d_out), d_scales, num_tokens, topk, hidden, slices, rows);
-  return hipGetLastError();
+hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, void* d_out,
+                           void* d_scales, int64_t rows, int num_tokens, int topk, int hidden,
+                           int max_blocks, hipStream_t stream) {
+  return launch_payload(dtype, d_x, TableRows{d_pos, topk, rows}, d_out, d_scales, num_tokens,
+                        hidden, max_blocks, stream);
+}
+
+hipError_t launch_dispatch_fixed(int dtype, const void* d_x, const int32_t* d_idx,
+                                 int num_tokens, int topk, int num_experts, int capacity,
+                                 int32_t* d_pos, int32_t* d_counts, int32_t* d_status,
+                                 void* d_out, void* d_scales, int hidden, int max_blocks,
+                                 hipStream_t stream) {
+  const FixedCapacityRows src{d_idx, topk, num_experts, capacity, d_pos, d_counts, d_status};
+  return launch_payload(dtype, d_x, src, d_out, d_scales, num_tokens, hidden, max_blocks, stream);
 }
 
 }  // namespace moe

@@ -56,16 +56,25 @@ hipError_t launch_layout(const int32_t* d_idx, int num_tokens, int topk, int num
 hipError_t launch_rank_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,
                               int num_ranks, const RankArrays& a, hipStream_t stream);
 
-// `rows` is the row count of the expert-major buffer; rows outside it are
-// never read or written, whatever pos holds.
-// `max_blocks` > 0 caps the grid (see item_grid).
-hipError_t launch_dispatch_bf16(const void* d_x, const int32_t* d_pos, void* d_out,
-                                int64_t rows, int num_tokens, int topk, int hidden,
-                                int max_blocks, hipStream_t stream);
+// Dispatch of dtype (moe_dtype_t) through the table d_pos[T, k]. `rows` is
+// the row count of the expert-major buffer; rows outside it are never read
+// or written, whatever pos holds. `max_blocks` > 0 caps the grid (item_grid).
+hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, void* d_out,
+                           void* d_scales, int64_t rows, int num_tokens, int topk, int hidden,
+                           int max_blocks, hipStream_t stream);
 
-hipError_t launch_dispatch_fp8(const void* d_x, const int32_t* d_pos, void* d_out,
-                               float* d_scales, int64_t rows, int num_tokens, int topk,
-                               int hidden, int max_blocks, hipStream_t stream);
+// Fixed-capacity (decode-time) layout and dispatch in one launch: rows
+// [e*capacity, (e+1)*capacity) belong to expert e. Records d_pos [T, k],
+// d_counts [E] and d_status [4] (invalid, placed, T, dropped).
+hipError_t launch_dispatch_fixed(int dtype, const void* d_x, const int32_t* d_idx,
+                                 int num_tokens, int topk, int num_experts, int capacity,
+                                 int32_t* d_pos, int32_t* d_counts, int32_t* d_status,
+                                 void* d_out, void* d_scales, int hidden, int max_blocks,
+                                 hipStream_t stream);
+
+// Router: top-k of each token's logits and the weights (score: moe_score_t).
+hipError_t launch_route(const float* d_logits, int num_tokens, int num_experts, int topk,
+                        int score, int32_t* d_idx, float* d_w, hipStream_t stream);
 
 hipError_t launch_combine(const void* d_y, int64_t rows, const float* d_w, const int32_t* d_pos,
                           void* d_out, int num_tokens, int topk, int hidden, int max_blocks,
@@ -84,10 +93,6 @@ inline dim3 item_grid(int64_t num_items, int max_blocks) {
   if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
   return dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks));
 }
-
-hipError_t launch_dispatch_mxfp8(const void* d_x, const int32_t* d_pos, void* d_out,
-                                 void* d_scales, int64_t rows, int num_tokens, int topk,
-                                 int hidden, int max_blocks, hipStream_t stream);
 
 hipError_t launch_rank_meta(const int32_t* d_idx, const float* d_w, const int32_t* d_slot_row,
                             int num_tokens, int topk, int num_experts, int num_ranks, int64_t rows,

@@ -67,6 +67,7 @@ extern "C" {
 #define MOE_EP_MAX_TOPK 32
 #define MOE_EP_FP8_BLOCK 128
 #define MOE_EP_STATUS_WORDS 4
+#define MOE_EP_LL_MAX_TOKENS 1024 /* num_tokens limit of the decode-time calls */
 
 typedef enum {
   MOE_OK = 0,
@@ -81,6 +82,11 @@ typedef enum {
   MOE_DTYPE_FP8_E4M3 = 1,  /* E4M3 bytes + one fp32 scale per 128 channels */
   MOE_DTYPE_MXFP8_E4M3 = 2 /* OCP MX: E4M3 bytes + one E8M0 byte per 32 channels */
 } moe_dtype_t;
+
+typedef enum {
+  MOE_SCORE_SOFTMAX = 0, /* w_j = exp(l_j) / sum_i exp(l_i) over the selected experts */
+  MOE_SCORE_SIGMOID = 1  /* w_j = s_j / sum_i s_i, s = 1 / (1 + exp(-l)) */
+} moe_score_t;
 
 /* Fixed at handle creation. max_tokens bounds num_tokens of every layout. */
 typedef struct {
@@ -217,6 +223,54 @@ int moe_combine_ranks(moe_handle_t h, const void* d_y, int64_t y_rows, void* d_o
  * Numbers"). Results are bit-identical for every cap. Negative values are
  * MOE_ERR_INVALID_ARG. Host-side only; enqueues nothing. */
 int moe_set_max_workgroups(moe_handle_t h, int32_t max_workgroups);
+
+/* Router: top-k expert selection and combine weights, the step that produces
+ * topk_idx / topk_w for the layout calls. Each token activates the top-k of
+ * the experts ("Inside the Nebius + PyTorch DeepSeek V3 recipe", section
+ * "Mixture-of-experts and wide expert parallelism"); the pages fix no tie
+ * rule or gate, so: the k largest logits in descending order, equal logits
+ * to the lower expert id (-0 equals +0); weights by `score` (moe_score_t)
+ * over the selected experts, computed in fp32 (expf, IEEE division).
+ * d_logits fp32 [num_tokens, num_experts] row-major (finite values; a NaN
+ * gives NaN weights, ids stay in range); d_topk_idx int32 and d_topk_w fp32
+ * [num_tokens, topk], written by this call. num_tokens in [0, max_tokens]. */
+int moe_route(moe_handle_t h, const float* d_logits, int32_t num_tokens, int score,
+              int32_t* d_topk_idx, float* d_topk_w, hipStream_t stream);
+
+/* Decode-time dispatch: layout and payload in one launch, into a buffer whose
+ * shape does not depend on the routing -- the regime of DeepEP's low-latency
+ * kernel family ("Inside the Nebius + PyTorch DeepSeek V3 recipe", section
+ * "DeepEP"). Expert e owns rows [e*capacity, (e+1)*capacity) of d_out; a
+ * slot's row is e*capacity + its rank among the slots routed to e in (token,
+ * slot) order; a slot ranked capacity or more is dropped (no row, no combine
+ * term, counted in status[3]); ids outside [0, E) are skipped (status[0]).
+ * num_tokens in [0, min(max_tokens, MOE_EP_LL_MAX_TOKENS)] (each wavefront
+ * counts over all earlier slots, O(num_tokens * topk)); capacity >= 1;
+ * out_rows >= num_experts * capacity. dtype, d_out and d_scales as in
+ * moe_dispatch (scales rows = out_rows). Rows no slot maps to are not
+ * written. Records the positions and per-expert counts in the handle (see
+ * moe_ll_view) for moe_ll_combine; independent of moe_dispatch_layout. */
+int moe_ll_dispatch(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_tokens,
+                    int32_t capacity, const void* d_x, int dtype, void* d_out, void* d_scales,
+                    int64_t out_rows, hipStream_t stream);
+
+typedef struct {
+  int32_t* pos;    /* [num_tokens * topk] row of each slot, -1 if skipped or dropped */
+  int32_t* counts; /* [num_experts] rows received per expert (<= capacity) */
+  int32_t* status; /* [4] invalid slots, placed slots, num_tokens, dropped slots */
+  int32_t num_tokens;
+  int32_t capacity;
+  int64_t rows;    /* num_experts * capacity */
+} moe_ll_view_t;
+
+/* Device pointers of the last moe_ll_dispatch (MOE_ERR_STATE before one). */
+int moe_ll_view(moe_handle_t h, moe_ll_view_t* out);
+
+/* Combine after moe_ll_dispatch: as moe_combine, over the fixed-capacity
+ * rows; y bf16 [y_rows, hidden], y_rows >= num_experts * capacity. Dropped
+ * and skipped slots contribute nothing. */
+int moe_ll_combine(moe_handle_t h, const void* d_y, int64_t y_rows, const float* d_w,
+                   void* d_out, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(int status);

@@ -62,3 +62,20 @@ def assert_combine_close(got_bits, ref_bits, mag, k, extra=None):
 
 def oracle_layout(idx, E, R):
     return oracle.layout(idx, E, R)
+
+
+def router_weight_tol(logits, idx, w_ref):
+    """Allowance for fp32 router weights against the oracle's (fp64, rounded once).
+
+    Per weight, relative to w_ref, in units of 2^-24: the logit difference
+    l_j - l_max rounds with error up to |l_j - l_max| units of relative error
+    in exp (and the same for the largest one in the sum), expf is within one
+    fp32 ulp (2 units), the fp32 butterfly sum of at most 32 positive terms
+    adds at most 5 levels (5 units), the division and the oracle's rounding one
+    unit each; the sigmoid's 1 + e and reciprocal add two. That is at most
+    2 + 2 + 5 + 1 + 1 + 2 + 2*D = 13 + 2D units for D = max_j |l_j - l_max|; the
+    bound allows 16 + 2D, plus 1e-30 absolute for terms that underflow.
+    """
+    sel = np.take_along_axis(np.asarray(logits, np.float64), idx.astype(np.int64), axis=1)
+    D = np.max(np.abs(sel - sel[:, :1]), axis=1, keepdims=True)
+    return 2.0 ** -24 * (16.0 + 2.0 * D) * np.abs(w_ref.astype(np.float64)) + 1e-30

@@ -39,11 +39,13 @@ def test_library_exports_every_declared_function(lib):
 
 def test_header_constants_match_binding():
     text = open(HEADER).read()
-    for name in ("MOE_EP_MAX_EXPERTS", "MOE_EP_MAX_TOPK", "MOE_EP_FP8_BLOCK", "MOE_EP_STATUS_WORDS"):
+    for name in ("MOE_EP_MAX_EXPERTS", "MOE_EP_MAX_TOPK", "MOE_EP_FP8_BLOCK", "MOE_EP_STATUS_WORDS",
+                 "MOE_EP_LL_MAX_TOKENS"):
         m = re.search(rf"#define {name} (\d+)", text)
         assert m and int(m.group(1)) == getattr(_lib, name)
     for name in ("MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_STATE", "MOE_ERR_HIP",
-                 "MOE_DTYPE_BF16", "MOE_DTYPE_FP8_E4M3", "MOE_DTYPE_MXFP8_E4M3"):
+                 "MOE_DTYPE_BF16", "MOE_DTYPE_FP8_E4M3", "MOE_DTYPE_MXFP8_E4M3",
+                 "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID"):
         m = re.search(rf"\b{name} = (\d+)", text)
         assert m and int(m.group(1)) == getattr(_lib, name), name
 
@@ -53,8 +55,10 @@ def test_workspace_bytes(lib):
     n = lib.moe_workspace_bytes(ctypes.byref(c))
     slots = 4096 * 8
     # expert layout: pos + src_idx + 16 histograms of 256 experts; rank layout:
-    # slot_row + rank_pos [T, 8] + src [T * 8] + 16 histograms of 8 ranks; small arrays
-    need = 2 * 4 * slots + 16 * 256 * 4 + 4 * slots + 4 * 4096 * 8 + 4 * 4096 * 8 + 16 * 8 * 4
+    # slot_row + rank_pos [T, 8] + src [T * 8] + 16 histograms of 8 ranks; decode-time
+    # layout: pos [1024 * 8] + counts [256]; small arrays
+    need = (2 * 4 * slots + 16 * 256 * 4 + 4 * slots + 4 * 4096 * 8 + 4 * 4096 * 8 + 16 * 8 * 4
+            + 4 * 1024 * 8 + 4 * 256)
     assert need <= n < need + 16 * 1024
     assert n % 256 == 0
     zero = lib.moe_workspace_bytes(ctypes.byref(cfg(0)))
@@ -140,6 +144,57 @@ def test_rank_calls_need_a_rank_layout(lib):
     assert lib.moe_rank_layout(h, fake, 129, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_rank_layout(h, None, 3, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_rank_layout(None, fake, 3, None) == _lib.MOE_ERR_INVALID_ARG
+    lib.moe_handle_destroy(h)
+
+
+def test_route_arguments(lib):
+    h = make_handle(lib)
+    fake = ctypes.c_void_p(1 << 24)
+    assert lib.moe_route(h, fake, 129, 0, fake, fake, None) == _lib.MOE_ERR_INVALID_ARG
+    assert "num_tokens" in lib.moe_last_error().decode()
+    assert lib.moe_route(h, fake, 4, 7, fake, fake, None) == _lib.MOE_ERR_INVALID_ARG
+    assert "score" in lib.moe_last_error().decode()
+    assert lib.moe_route(h, None, 4, 0, fake, fake, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(h, ctypes.c_void_p((1 << 24) + 2), 4, 1, fake, fake, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, fake, 4, 0, fake, fake, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(h, None, 0, 0, None, None, None) == _lib.MOE_OK     # nothing to do
+    lib.moe_handle_destroy(h)
+
+
+def test_decode_time_calls_arguments(lib):
+    h = make_handle(lib, cfg(T=2000, H=256, k=2, E=8, R=2))
+    fake = ctypes.c_void_p(1 << 24)
+    # state before any decode-time dispatch
+    assert lib.moe_ll_combine(h, fake, 1 << 20, fake, fake, None) == _lib.MOE_ERR_STATE
+    assert "moe_ll_dispatch" in lib.moe_last_error().decode()
+    v = _lib.MoeLlView()
+    assert lib.moe_ll_view(h, ctypes.byref(v)) == _lib.MOE_ERR_STATE
+    # token limit is min(max_tokens, MOE_EP_LL_MAX_TOKENS)
+    assert lib.moe_ll_dispatch(h, fake, 1025, 4, fake, 0, fake, None, 1 << 20, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    assert "MOE_EP_LL_MAX_TOKENS" in lib.moe_last_error().decode()
+    assert lib.moe_ll_dispatch(h, fake, 16, 0, fake, 0, fake, None, 1 << 20, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    assert "capacity" in lib.moe_last_error().decode()
+    assert lib.moe_ll_dispatch(h, fake, 16, 4, fake, 0, fake, None, 31, None) == \
+        _lib.MOE_ERR_INVALID_ARG                                   # 8 experts * 4 rows needed
+    assert "out_rows" in lib.moe_last_error().decode()
+    assert lib.moe_ll_dispatch(h, fake, 16, 4, fake, 9, fake, None, 32, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_ll_dispatch(h, fake, 16, 4, fake, 1, fake, None, 32, None) == \
+        _lib.MOE_ERR_INVALID_ARG                                   # FP8 without scales
+    assert lib.moe_ll_dispatch(h, fake, 16, 4, ctypes.c_void_p((1 << 24) + 8), 0, fake, None, 32,
+                               None) == _lib.MOE_ERR_INVALID_ARG   # x not 16-byte aligned
+    assert lib.moe_ll_dispatch(h, fake, 16, 1 << 28, fake, 0, fake, None, 1 << 40, None) == \
+        _lib.MOE_ERR_UNSUPPORTED
+    assert lib.moe_ll_dispatch(None, fake, 16, 4, fake, 0, fake, None, 32, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    lib.moe_handle_destroy(h)
+    h = make_handle(lib, cfg(T=64, H=200, k=2, E=8, R=2))
+    assert lib.moe_ll_dispatch(h, fake, 16, 4, fake, 2, fake, fake, 32, None) == \
+        _lib.MOE_ERR_UNSUPPORTED
+    assert "multiple of 128" in lib.moe_last_error().decode()
     lib.moe_handle_destroy(h)
 
 

@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from combine_moe_dispatch_02_amd import Handle
-from workloads import CONFIGS, bf16_bits_from_f32, make_workload
+from workloads import CONFIGS, bf16_bits_from_f32
+from routed import make_workload
 from gpu_util import dev_bf16, dev_i32, host_bits
 
 pytestmark = pytest.mark.gpu

@@ -14,7 +14,8 @@ import torch
 
 import oracle
 from combine_moe_dispatch_02_amd import Handle, MoeError
-from workloads import CONFIGS, make_expert_outputs, make_workload
+from workloads import CONFIGS, make_expert_outputs
+from routed import make_workload
 from gpu_util import (assert_combine_close, assert_layout_equal, dev_bf16, dev_f32, dev_i32,
                       host_bits, layout_on_gpu)
 

@@ -10,7 +10,8 @@ import pytest
 from hypothesis import given, settings, strategies as st
 
 from oracle import layout
-from workloads import CONFIGS, make_workload
+from workloads import CONFIGS
+from routed import make_workload
 from conftest import load_golden
 
 

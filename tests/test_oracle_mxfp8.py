@@ -8,7 +8,8 @@ import torch
 
 from oracle.codecs import bf16_decode, e4m3_decode
 from oracle.moe import dequant_mxfp8, dispatch_mxfp8, e8m0_decode, layout, quantize_mxfp8_rows
-from workloads import bf16_bits_from_f32, make_workload
+from workloads import bf16_bits_from_f32
+from routed import make_workload
 from conftest import hexint, load_golden
 
 

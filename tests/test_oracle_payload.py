@@ -16,7 +16,8 @@ import torch
 from oracle import combine, dequant_fp8, dispatch_bf16, dispatch_fp8, layout
 from oracle.codecs import bf16_decode, e4m3_decode
 from oracle.moe import quantize_fp8_rows
-from workloads import bf16_bits_from_f32, make_expert_outputs, make_workload
+from workloads import bf16_bits_from_f32, make_expert_outputs
+from routed import make_workload
 from conftest import combine_tolerance, hexint, load_golden
 
 

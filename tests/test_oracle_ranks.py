@@ -12,7 +12,8 @@ from hypothesis import given, settings, strategies as st
 
 import oracle
 from oracle.codecs import bf16_decode
-from workloads import CONFIGS, make_expert_outputs, make_workload
+from workloads import CONFIGS, make_expert_outputs
+from routed import make_workload
 from conftest import combine_tolerance, load_golden
 
 

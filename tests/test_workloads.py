@@ -1,33 +1,39 @@
-"""Checks of the seeded input generators (shapes, determinism, router output)."""
+"""Checks of the seeded input generators (shapes, determinism, logit
+distributions) and of the routed workloads the tests build from them."""
 import numpy as np
 import pytest
 
-from workloads import CONFIGS, make_expert_outputs, make_workload
+import workloads
+from workloads import CONFIGS, make_expert_outputs
+from routed import make_workload
 
 
 @pytest.mark.parametrize("shape", CONFIGS, ids=lambda s: s.name)
-def test_workload_shapes_and_router(shape):
-    wl = make_workload(shape.name)
+def test_workload_shapes(shape):
+    raw = workloads.make_workload(shape.name)
     T, H, E, k = shape.tokens, shape.hidden, shape.experts, shape.topk
-    assert wl.x_bits.shape == (T, H) and wl.x_bits.dtype == np.uint16
+    assert raw.x_bits.shape == (T, H) and raw.x_bits.dtype == np.uint16
+    assert raw.logits.shape == (T, E) and raw.logits.dtype == np.float32
+    assert raw.topk_idx is None and raw.topk_w is None      # the generator does not route
+    assert raw.seed == 1000 + CONFIGS.index(shape)
+    wl = make_workload(shape.name)
     assert wl.topk_idx.shape == (T, k) and wl.topk_idx.dtype == np.int32
     assert wl.topk_w.shape == (T, k) and wl.topk_w.dtype == np.float32
-    assert wl.topk_idx.min() >= 0 and wl.topk_idx.max() < E
-    # top-k picks k distinct experts per token
-    s = np.sort(wl.topk_idx, axis=1)
-    assert np.all(np.diff(s, axis=1) > 0)
-    # normalised weights, descending with the router order
-    assert np.allclose(wl.topk_w.sum(axis=1), 1.0, atol=1e-6)
-    assert np.all(np.diff(wl.topk_w, axis=1) <= 0)
-    assert wl.seed == 1000 + CONFIGS.index(shape)
+    assert np.array_equal(wl.x_bits, raw.x_bits) and np.array_equal(wl.logits, raw.logits)
+
+
+def test_hidden_does_not_change_the_logits():
+    a = workloads.make_workload("deepseekv3", tokens=32)
+    b = workloads.make_workload("deepseekv3", tokens=32, hidden=128)
+    assert np.array_equal(a.logits, b.logits)
 
 
 def test_workload_deterministic():
-    a = make_workload("deepseek16b", tokens=64)
-    b = make_workload("deepseek16b", tokens=64)
-    assert np.array_equal(a.x_bits, b.x_bits) and np.array_equal(a.topk_idx, b.topk_idx)
-    c = make_workload("deepseek16b", tokens=64, seed=1)
-    assert not np.array_equal(a.topk_idx, c.topk_idx)
+    a = workloads.make_workload("deepseek16b", tokens=64)
+    b = workloads.make_workload("deepseek16b", tokens=64)
+    assert np.array_equal(a.x_bits, b.x_bits) and np.array_equal(a.logits, b.logits)
+    c = workloads.make_workload("deepseek16b", tokens=64, seed=1)
+    assert not np.array_equal(a.logits, c.logits)
     assert np.array_equal(make_expert_outputs(8, 16, 3), make_expert_outputs(8, 16, 3))
 
 

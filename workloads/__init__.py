@@ -17,10 +17,12 @@ Workload shapes follow the pages:
   * The cryptojournalpost Hybrid-EP news item, section "Efficiency Numbers":
     a Qwen3-235B run, used here for the skewed, larger-T configuration.
 
-Router outputs are inputs to the hot path, so the router itself lives here:
-top-k by a stable descending sort of the logits (ties go to the lower expert
-id), and fp32 weights normalised over the k selected experts (softmax, or
-sigmoid scores divided by their sum for the DeepSeek-V3-like shapes).
+The generator draws router logits, not routing decisions: the top-k
+selection and its weights are part of the method (the library has a router
+kernel, the oracle a router definition), so callers route the logits
+themselves -- the tests through the oracle, the benchmark through the
+library. Each shape names its weighting ("softmax", or "sigmoid" scores
+divided by their sum for the DeepSeek-V3-like shapes).
 """
 from __future__ import annotations
 
@@ -28,8 +30,7 @@ import dataclasses
 
 import numpy as np
 
-__all__ = ["Workload", "CONFIGS", "make_workload", "make_expert_outputs",
-           "route", "bf16_bits_from_f32"]
+__all__ = ["Workload", "CONFIGS", "make_workload", "make_expert_outputs", "bf16_bits_from_f32"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,9 +63,10 @@ ZIPF_S = 1.2
 class Workload:
     shape: Shape
     seed: int
-    x_bits: np.ndarray      # uint16 [T, H], bf16 bit patterns
-    topk_idx: np.ndarray    # int32  [T, k]
-    topk_w: np.ndarray      # float32 [T, k]
+    x_bits: np.ndarray               # uint16 [T, H], bf16 bit patterns
+    logits: np.ndarray               # float32 [T, E], router logits
+    topk_idx: np.ndarray | None = None   # int32 [T, k], filled in by the caller's router
+    topk_w: np.ndarray | None = None     # float32 [T, k]
 
     @property
     def T(self):
@@ -80,22 +82,6 @@ def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     import torch
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-
-
-def route(logits: np.ndarray, k: int, weights: str):
-    """Top-k of each row (stable descending order) and normalised fp32 weights."""
-    logits = np.asarray(logits, dtype=np.float32)
-    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
-    sel = np.take_along_axis(logits, order, axis=1).astype(np.float32)
-    if weights == "softmax":
-        z = np.exp(sel - sel.max(axis=1, keepdims=True), dtype=np.float32)
-        w = z / z.sum(axis=1, keepdims=True, dtype=np.float32)
-    elif weights == "sigmoid":
-        s = (np.float32(1.0) / (np.float32(1.0) + np.exp(-sel, dtype=np.float32))).astype(np.float32)
-        w = s / s.sum(axis=1, keepdims=True, dtype=np.float32)
-    else:
-        raise ValueError(weights)
-    return order.astype(np.int32), w.astype(np.float32)
 
 
 def _logits(rng, shape: Shape) -> np.ndarray:
@@ -131,9 +117,8 @@ def make_workload(name_or_index, seed: int | None = None, tokens: int | None = N
         seed = 1000 + index
     rng = np.random.default_rng(seed)
     logits = _logits(rng, shape)
-    idx, w = route(logits, shape.topk, shape.weights)
     x = rng.standard_normal((shape.tokens, shape.hidden), dtype=np.float32)
-    return Workload(shape, seed, bf16_bits_from_f32(x), idx, w)
+    return Workload(shape, seed, bf16_bits_from_f32(x), logits)
 
 
 def make_expert_outputs(rows: int, hidden: int, seed: int) -> np.ndarray:
