@@ -86,6 +86,7 @@ struct TableRows {
 };
 
 // Fixed-capacity layout, computed on the fly (decode-time dispatch).
+constexpr int kRankLoads = 16;
 struct FixedCapacityRows {
   static constexpr bool kCountsBlock = true;
   const int32_t* idx;   // [T, k] expert ids
@@ -102,15 +103,25 @@ struct FixedCapacityRows {
       e[jj] = idx[base + (j0 + jj < topk ? j0 + jj : topk - 1)];
       rank[jj] = 0;
     }
-    // Rank of slot s = number of earlier slots with the same id.
+    // Rank of slot s = number of earlier slots with the same id. The ids are
+    // read kRankLoads chunks of 64 at a time, so those loads are in flight
+    // together instead of one dependent load per chunk.
     const int lane = threadIdx.x & 63;
     const int last = base + (j0 + kSlotBatch < topk ? j0 + kSlotBatch : topk);
-    for (int c = 0; c < last; c += 64) {
-      const int s = c + lane;
-      const int id = s < last ? idx[s] : -1;
+    for (int c = 0; c < last; c += 64 * kRankLoads) {
+      int id[kRankLoads];
 #pragma unroll
-      for (int jj = 0; jj < kSlotBatch; ++jj)
-        rank[jj] += __popcll(__ballot(id == e[jj] && s < base + j0 + jj));
+      for (int q = 0; q < kRankLoads; ++q) {
+        const int s = c + q * 64 + lane;
+        id[q] = s < last ? idx[s] : -1;
+      }
+#pragma unroll
+      for (int q = 0; q < kRankLoads; ++q) {
+        const int s = c + q * 64 + lane;
+#pragma unroll
+        for (int jj = 0; jj < kSlotBatch; ++jj)
+          rank[jj] += __popcll(__ballot(id[q] == e[jj] && s < base + j0 + jj));
+      }
     }
     int mine = -1;
 #pragma unroll

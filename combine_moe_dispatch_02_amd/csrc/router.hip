@@ -8,13 +8,14 @@
 // scores divided by their sum (the DeepSeek-V3-style gate, no extra scale).
 //
 // One wavefront per token, no LDS and no barrier. Lane l holds the logits of
-// experts l, l+64, l+128, ... as 64-bit keys: the high word is the logit's
-// bit pattern mapped to an unsigned order (sign-magnitude -> biased), the low
-// word ~expert, so the unsigned maximum is the largest logit and, among equal
-// ones, the lowest id. Each of the k rounds takes the wavefront maximum of
-// the keys (6 butterfly steps of two 32-bit shuffles), clears the winner's
-// key in its owner lane, and leaves the winner with lane `round`. The weights
-// are then computed by lanes 0..k-1 in fp32 and summed by a butterfly.
+// experts l, l+64, l+128, ... as unsigned order keys (the bit pattern mapped
+// so that unsigned order is numeric order, -0 folded onto +0). Each of the k
+// rounds: every lane takes its best live key (the lower id on ties), the
+// wavefront maximum is formed with four DPP steps inside each 16-lane row
+// and four readlanes across rows (so it is a scalar), and the lowest expert
+// id holding it is read off ballots. The winner's owner lane retires it, and
+// lane `round` keeps it. Lanes 0..k-1 then compute the weights in fp32 and a
+// DPP row sum adds them in a fixed order.
 #include "moe_internal.h"
 
 namespace moe {
@@ -29,21 +30,39 @@ __device__ __forceinline__ float from_order_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, 64);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, 64);
-    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// DPP controls (GFX9 encoding): quad permutations and row mirrors. After the
+// four steps every lane of a 16-lane row holds the row's reduction.
+constexpr int kQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i within each 8
+constexpr int kRowMirror = 0x140;      // lane i <-> 15 - i within each 16
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Maximum over the wavefront, returned as a scalar.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax(v, dpp<kQuadSwap1>(v));
+  v = umax(v, dpp<kQuadSwap2>(v));
+  v = umax(v, dpp<kRowHalfMirror>(v));
+  v = umax(v, dpp<kRowMirror>(v));
+  return umax(umax(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+              umax(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Sum of lanes 0..31 (the rest hold 0), in a fixed order, as a scalar.
+__device__ __forceinline__ float sum_lanes_0_31(float v) {
+  v += __uint_as_float(dpp<kQuadSwap1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kQuadSwap2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kRowHalfMirror>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kRowMirror>(__float_as_uint(v)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
 }
 
 // kPer: logits per lane (experts <= 64 * kPer).
@@ -55,36 +74,53 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int lane = threadIdx.x & 63;
   for (int t = blockIdx.x * 4 + wave_index(); t < num_tokens; t += gridDim.x * 4) {
     const float* row = logits + static_cast<size_t>(t) * num_experts;
-    uint64_t key[kPer];
+    uint32_t key[kPer];
+    bool live[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = i * 64 + lane;
-      key[i] = e < num_experts
-                   ? (static_cast<uint64_t>(order_bits(row[e])) << 32) | (~static_cast<uint32_t>(e))
-                   : 0ull;   // below every real key
+      live[i] = e < num_experts;
+      key[i] = live[i] ? order_bits(row[e]) : 0u;
     }
     float sel_v = 0.0f;
     int sel_e = 0;
     for (int r = 0; r < topk; ++r) {
-      uint64_t best = key[0];
+      bool have = false;
+      uint32_t best = 0u;
+      int bi = 0;
 #pragma unroll
-      for (int i = 1; i < kPer; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
-      const int e = static_cast<int>(~static_cast<uint32_t>(best));
+      for (int i = 0; i < kPer; ++i) {
+        if (live[i] && (!have || key[i] > best)) {
+          best = key[i];
+          bi = i;
+          have = true;
+        }
+      }
+      const uint32_t top = wave_max_u32(have ? best : 0u);
+      const bool tied = have && best == top;
+      int e = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const uint64_t m = __ballot(tied && bi == i);
+        if (m) {
+          e = i * 64 + __builtin_ctzll(m);
+          break;
+        }
+      }
       if (lane == (e & 63)) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i)
-          if (i == (e >> 6)) key[i] = 0ull;
+          if (i == (e >> 6)) live[i] = false;
       }
       if (lane == r) {
-        sel_v = from_order_bits(static_cast<uint32_t>(best >> 32));
+        sel_v = from_order_bits(top);
         sel_e = e;
       }
     }
-    const float top = __shfl(sel_v, 0, 64);   // the largest selected logit
+    const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
     float z = 0.0f;
     if (lane < topk) z = sigmoid ? 1.0f / (1.0f + expf(-sel_v)) : expf(sel_v - top);
-    const float sum = wave_sum(z);
+    const float sum = sum_lanes_0_31(z);
     if (lane < topk) {
       idx[static_cast<size_t>(t) * topk + lane] = sel_e;
       w[static_cast<size_t>(t) * topk + lane] = z / sum;
