@@ -46,6 +46,10 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
+        # never leave a library built from older sources in place
+        for stale in (LIB_PATH, tmp):
+            if os.path.exists(stale):
+                os.remove(stale)
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
