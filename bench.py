@@ -391,7 +391,24 @@ def main():
         decode["combine_us"] = sustained_us(
             lambda i: hd.combine(D(i)["std"], D(i)["w"], out=D(i)["c"]), args.sustained_iters)
         decode["payload_bytes_bf16"] = 2 * Td * H + 2 * Td * k * H
-        del dsets, hd
+
+        # The whole decode step (router -> decode-time dispatch -> combine of the
+        # dispatched rows), eagerly and replayed as one captured HIP graph.
+        g0 = dsets[0]
+
+        def decode_step():
+            hd.route(g0["lg"], s.weights, topk_idx=g0["idx"], topk_w=g0["w"])
+            hd.ll_dispatch(g0["idx"], g0["x"], C, out=g0["out"])
+            hd.ll_combine(g0["out"], g0["w"], out=g0["c"])
+        decode_step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode_step()
+        torch.cuda.synchronize()
+        decode["step_eager_us"] = sustained_us(lambda i: decode_step(), args.sustained_iters)
+        decode["step_graph_us"] = sustained_us(lambda i: graph.replay(), args.sustained_iters)
+        del graph, dsets, hd
 
     dominant = max(("dispatch_bf16", "dispatch_fp8", "combine"), key=lambda n: per_op[n]["us_mean"])
     achieved = per_op[dominant]["GBps"]
