@@ -96,6 +96,7 @@ struct TableRows {
 
 // Fixed-capacity layout, computed on the fly (decode-time dispatch).
 constexpr int kRankLoads = 16;
+constexpr int kCountLoads = 8;
 struct FixedCapacityRows {
   static constexpr bool kCountsBlock = true;
   const int32_t* idx;   // [T, k] expert ids
@@ -112,25 +113,33 @@ struct FixedCapacityRows {
       e[jj] = idx[base + (j0 + jj < topk ? j0 + jj : topk - 1)];
       rank[jj] = 0;
     }
-    // Rank of slot s = number of earlier slots with the same id. The ids are
-    // read kRankLoads chunks of 64 at a time, so those loads are in flight
-    // together instead of one dependent load per chunk.
+    // Rank of slot (t, j) = number of earlier slots with the same id: the
+    // slots of earlier tokens, [0, base), plus slots j' < j of this token.
+    // Each lane counts matches in its registers (one compare and one add per
+    // id and slot; kRankLoads chunks of 64 ids in flight), then one wavefront
+    // sum per slot.
     const int lane = threadIdx.x & 63;
-    const int last = base + (j0 + kSlotBatch < topk ? j0 + kSlotBatch : topk);
-    for (int c = 0; c < last; c += 64 * kRankLoads) {
+    uint32_t cnt[kSlotBatch];
+#pragma unroll
+    for (int jj = 0; jj < kSlotBatch; ++jj) cnt[jj] = 0u;
+    for (int c = 0; c < base; c += 64 * kRankLoads) {
       int id[kRankLoads];
 #pragma unroll
       for (int q = 0; q < kRankLoads; ++q) {
         const int s = c + q * 64 + lane;
-        id[q] = s < last ? idx[s] : -1;
+        id[q] = idx[s < base ? s : 0];
+        if (s >= base) id[q] = -1;
       }
 #pragma unroll
-      for (int q = 0; q < kRankLoads; ++q) {
-        const int s = c + q * 64 + lane;
+      for (int q = 0; q < kRankLoads; ++q)
 #pragma unroll
-        for (int jj = 0; jj < kSlotBatch; ++jj)
-          rank[jj] += __popcll(__ballot(id[q] == e[jj] && s < base + j0 + jj));
-      }
+        for (int jj = 0; jj < kSlotBatch; ++jj) cnt[jj] += id[q] == e[jj] ? 1u : 0u;
+    }
+    const int own = idx[base + (lane < topk ? lane : 0)];   // this token's ids, lanes < topk
+#pragma unroll
+    for (int jj = 0; jj < kSlotBatch; ++jj) {
+      cnt[jj] += (lane < j0 + jj && own == e[jj]) ? 1u : 0u;
+      rank[jj] = static_cast<int>(wave_sum_u32(cnt[jj]));
     }
     int mine = -1;
 #pragma unroll
@@ -154,10 +163,23 @@ struct FixedCapacityRows {
     __syncthreads();
     const int slots = num_tokens * topk;
     int bad = 0;
-    for (int s = tid; s < slots; s += nthreads) {
-      const int id = idx[s];
-      if (static_cast<unsigned>(id) < static_cast<unsigned>(num_experts)) atomicAdd(&hist[id], 1);
-      else ++bad;
+    // kCountLoads ids per thread are loaded before any is counted, so the
+    // loads overlap instead of each waiting on the one before.
+    for (int base = 0; base < slots; base += nthreads * kCountLoads) {
+      int id[kCountLoads];
+#pragma unroll
+      for (int q = 0; q < kCountLoads; ++q) {
+        const int s = base + q * nthreads + tid;
+        id[q] = s < slots ? idx[s] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < kCountLoads; ++q) {
+        if (base + q * nthreads + tid >= slots) continue;
+        if (static_cast<unsigned>(id[q]) < static_cast<unsigned>(num_experts))
+          atomicAdd(&hist[id[q]], 1);
+        else
+          ++bad;
+      }
     }
     if (bad) atomicAdd(&tally[0], bad);
     __syncthreads();

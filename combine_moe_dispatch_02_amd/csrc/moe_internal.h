@@ -86,6 +86,44 @@ __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 }
 
+// Cross-lane reductions with DPP (GFX9 encoding): two quad permutations, then
+// the half-row and row mirrors, leave every lane of a 16-lane row holding the
+// row's reduction; four readlanes combine the rows into a scalar.
+constexpr int kDppQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within each 8
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15 - i within each 16
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Maximum of v over the wavefront, as a scalar.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_umax(v, dpp_u32<kDppQuadSwap1>(v));
+  v = dpp_umax(v, dpp_u32<kDppQuadSwap2>(v));
+  v = dpp_umax(v, dpp_u32<kDppRowHalfMirror>(v));
+  v = dpp_umax(v, dpp_u32<kDppRowMirror>(v));
+  return dpp_umax(dpp_umax(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                  dpp_umax(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Sum of v over the wavefront (modulo 2^32), as a scalar.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp_u32<kDppQuadSwap1>(v);
+  v += dpp_u32<kDppQuadSwap2>(v);
+  v += dpp_u32<kDppRowHalfMirror>(v);
+  v += dpp_u32<kDppRowMirror>(v);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 0)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 16)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 32)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 48));
+}
+
 // Grid for num_items wavefront work items: one workgroup per kItemWaves
 // items, or at most max_blocks workgroups (> 0), whose wavefronts then loop.
 inline dim3 item_grid(int64_t num_items, int max_blocks) {

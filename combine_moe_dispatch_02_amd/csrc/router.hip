@@ -13,7 +13,7 @@
 // rounds: every lane takes its best live key (the lower id on ties), the
 // wavefront maximum is formed with four DPP steps inside each 16-lane row
 // and four readlanes across rows (so it is a scalar), and the lowest expert
-// id holding it is read off ballots. The winner's owner lane retires it, and
+// id holding it by a second such reduction. The winner's owner lane retires it, and
 // lane `round` keeps it. Lanes 0..k-1 then compute the weights in fp32 and a
 // DPP row sum adds them in a fixed order.
 #include "moe_internal.h"
@@ -30,37 +30,13 @@ __device__ __forceinline__ float from_order_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// DPP controls (GFX9 encoding): quad permutations and row mirrors. After the
-// four steps every lane of a 16-lane row holds the row's reduction.
-constexpr int kQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i within each 8
-constexpr int kRowMirror = 0x140;      // lane i <-> 15 - i within each 16
-
-template <int kCtrl>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-// Maximum over the wavefront, returned as a scalar.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = umax(v, dpp<kQuadSwap1>(v));
-  v = umax(v, dpp<kQuadSwap2>(v));
-  v = umax(v, dpp<kRowHalfMirror>(v));
-  v = umax(v, dpp<kRowMirror>(v));
-  return umax(umax(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-              umax(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
-
-// Sum of lanes 0..31 (the rest hold 0), in a fixed order, as a scalar.
+// Sum of lanes 0..31 (the rest hold 0), in a fixed order, as a scalar (DPP
+// row sums as in wave_sum_u32, then rows 0 and 1).
 __device__ __forceinline__ float sum_lanes_0_31(float v) {
-  v += __uint_as_float(dpp<kQuadSwap1>(__float_as_uint(v)));
-  v += __uint_as_float(dpp<kQuadSwap2>(__float_as_uint(v)));
-  v += __uint_as_float(dpp<kRowHalfMirror>(__float_as_uint(v)));
-  v += __uint_as_float(dpp<kRowMirror>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppQuadSwap1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppQuadSwap2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppRowHalfMirror>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppRowMirror>(__float_as_uint(v)));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
 }
@@ -97,16 +73,11 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         }
       }
       const uint32_t top = wave_max_u32(have ? best : 0u);
+      // Lowest expert id holding the maximum: the maximum of ~id over the
+      // lanes that hold it (at least one does).
       const bool tied = have && best == top;
-      int e = 0;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const uint64_t m = __ballot(tied && bi == i);
-        if (m) {
-          e = i * 64 + __builtin_ctzll(m);
-          break;
-        }
-      }
+      const int e = static_cast<int>(
+          ~wave_max_u32(tied ? ~static_cast<uint32_t>(bi * 64 + lane) : 0u));
       if (lane == (e & 63)) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i)
