@@ -118,6 +118,54 @@ def test_edge_cases_all_ops(case):
     assert_combine_close(comb, ref_c, mag, k)
 
 
+@pytest.mark.parametrize("hidden", [8, 24, 520, 4104, 16384 + 8])
+def test_hidden_extremes_bf16(hidden):
+    """bf16 dispatch and combine from the smallest row (one 16-byte vector) to
+    rows whose last 512-channel slice holds a single vector."""
+    print(f"[hidden] bf16 H={hidden}", flush=True)
+    T, k, E, R = 700, 4, 32, 4
+    rng = np.random.default_rng(hidden)
+    idx = edge_ids(T, k, E, "invalid", seed=hidden)
+    x = rng.integers(0, 2 ** 16, size=(T, hidden), dtype=np.uint16) & np.uint16(0xBFFF)
+    h = Handle(T, hidden, k, E, R)
+    got = layout_on_gpu(h, idx)
+    ref = oracle.layout(idx, E, R)
+    assert_layout_equal(got, ref, T, k)
+    total = int(ref["offsets_e"][-1])
+    out = host_bits(h.dispatch(dev_bf16(x)))
+    assert np.array_equal(out[:total], oracle.dispatch_bf16(x, ref["pos"])[:total])
+    y = make_expert_outputs(T * k, hidden, seed=hidden + 1)
+    w = rng.uniform(-1, 1, size=(T, k)).astype(np.float32)
+    comb = host_bits(h.combine(dev_bf16(y), dev_f32(w)))
+    want, mag = oracle.combine(y, w, ref["pos"], return_magnitude=True)
+    assert_combine_close(comb, want, mag, k)
+
+
+@pytest.mark.parametrize("hidden", [128, 16384 + 128])
+def test_hidden_extremes_fp8(hidden):
+    """FP8 and MXFP8 dispatch at the smallest block-aligned row and a row whose
+    last 1024-channel slice holds one 128-channel block."""
+    print(f"[hidden] fp8 H={hidden}", flush=True)
+    T, k, E, R = 500, 8, 64, 8
+    rng = np.random.default_rng(hidden)
+    idx = edge_ids(T, k, E, "random", seed=hidden)
+    from workloads import bf16_bits_from_f32
+    xf = rng.standard_normal((T, hidden)).astype(np.float32) * np.exp2(
+        rng.integers(-30, 30, size=(T, hidden // 128, 1))).repeat(128, axis=2).reshape(T, hidden)
+    x = bf16_bits_from_f32(xf.astype(np.float32))
+    h = Handle(T, hidden, k, E, R)
+    h.layout(dev_i32(idx))
+    ref = oracle.layout(idx, E, R)
+    codes, scales = h.dispatch(dev_bf16(x), fp8=True)
+    rc, rs = oracle.dispatch_fp8(x, ref["pos"])
+    assert np.array_equal(host_bits(codes), rc)
+    assert np.array_equal(host_bits(scales).view(np.uint32), rs.view(np.uint32))
+    codes, scales = h.dispatch(dev_bf16(x), mxfp8=True)
+    rc, rs = oracle.dispatch_mxfp8(x, ref["pos"])
+    assert np.array_equal(host_bits(codes), rc)
+    assert np.array_equal(host_bits(scales), rs)
+
+
 def test_large_token_count_layout():
     T, k, E, R = 65536, 8, 256, 8
     idx = edge_ids(T, k, E, "random", seed=4)
