@@ -1,0 +1,100 @@
+"""Seeded random configurations through every entry point, against the oracle.
+
+Each case draws T, H, k, E, R, an id pattern (uniform, skewed, duplicates,
+invalid ids) and a fixed-capacity C, then checks the layout, bf16 / FP8 /
+MXFP8 dispatch, combine, the rank-deduplicated exchange and the decode-time
+path to the same bars as the dedicated tests (bit-exact, combine within the
+combine tolerance). The draws are fixed by the case seed.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from combine_moe_dispatch_02_amd import Handle
+from workloads import bf16_bits_from_f32, make_expert_outputs
+from gpu_util import (assert_combine_close, assert_layout_equal, dev_bf16, dev_f32, dev_i32,
+                      host_bits, layout_on_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def draw_case(seed):
+    rng = np.random.default_rng(10_000 + seed)
+    R = int(rng.choice([1, 2, 4, 8]))
+    E = R * int(rng.choice([1, 2, 3, 8, 16, 32]))
+    k = int(rng.integers(1, min(E, 32) + 1))
+    T = int(rng.choice([1, 2, 63, 64, 65, 257, 1000, 2049, 3001]))
+    H = 128 * int(rng.integers(1, 40))
+    pattern = str(rng.choice(["uniform", "skewed", "duplicates", "invalid"]))
+    if pattern == "uniform":
+        idx = rng.integers(0, E, size=(T, k))
+    elif pattern == "skewed":
+        p = np.arange(1, E + 1, dtype=np.float64) ** -1.5
+        idx = rng.choice(E, size=(T, k), p=p / p.sum())
+    elif pattern == "duplicates":
+        idx = rng.integers(0, max(1, E // 4), size=(T, k))
+    else:
+        idx = rng.integers(0, E, size=(T, k))
+        bad = rng.random((T, k)) < 0.25
+        idx[bad] = rng.choice(np.array([-1, E, 1 << 20, -(1 << 30)]), size=int(bad.sum()))
+    x = bf16_bits_from_f32((rng.standard_normal((T, H)) *
+                            np.exp2(rng.integers(-8, 8, size=(T, 1)))).astype(np.float32))
+    w = rng.uniform(-1, 1, size=(T, k)).astype(np.float32)
+    C = int(rng.integers(1, max(2, (T * k) // E + 3)))
+    return dict(T=T, H=H, k=k, E=E, R=R, pattern=pattern, idx=idx.astype(np.int32), x=x, w=w, C=C)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_config(seed):
+    c = draw_case(seed)
+    T, H, k, E, R, C = c["T"], c["H"], c["k"], c["E"], c["R"], c["C"]
+    idx, x, w = c["idx"], c["x"], c["w"]
+    print(f"[random {seed}] T={T} H={H} k={k} E={E} R={R} C={C} {c['pattern']}", flush=True)
+    h = Handle(T, H, k, E, R)
+    # standard layout and dispatches
+    got = layout_on_gpu(h, idx)
+    ref = oracle.layout(idx, E, R)
+    assert_layout_equal(got, ref, T, k)
+    n = int(ref["offsets_e"][-1])
+    dx = dev_bf16(x)
+    assert np.array_equal(host_bits(h.dispatch(dx))[:n], oracle.dispatch_bf16(x, ref["pos"])[:n])
+    q, s = h.dispatch(dx, fp8=True)
+    rq, rs = oracle.dispatch_fp8(x, ref["pos"])
+    assert np.array_equal(host_bits(q)[:n], rq[:n])
+    assert np.array_equal(host_bits(s)[:n].view(np.uint32), rs[:n].view(np.uint32))
+    q, s = h.dispatch(dx, mxfp8=True)
+    rq, rs = oracle.dispatch_mxfp8(x, ref["pos"])
+    assert np.array_equal(host_bits(q)[:n], rq[:n])
+    assert np.array_equal(host_bits(s)[:n], rs[:n])
+    # combine of independent expert outputs
+    y = make_expert_outputs(T * k, H, seed=seed)
+    comb = host_bits(h.combine(dev_bf16(y), dev_f32(w)))
+    want, mag = oracle.combine(y, w, ref["pos"], return_magnitude=True)
+    assert_combine_close(comb, want, mag, k)
+    # rank-deduplicated exchange
+    h.rank_layout(dev_i32(idx))
+    rl = oracle.rank_layout(idx, E, R)
+    rows, ridx, rw = h.dispatch_ranks(dx, dev_i32(idx), dev_f32(w))
+    want_rows, want_idx, want_w = oracle.dispatch_ranks(x, idx, w, E, R, rl)
+    m = int(rl["offsets_r"][-1])
+    assert np.array_equal(host_bits(rows)[:m], want_rows[:m])
+    assert np.array_equal(ridx.cpu().numpy()[:m], want_idx[:m])
+    assert np.array_equal(rw.cpu().numpy()[:m].view(np.uint32), want_w[:m].view(np.uint32))
+    part = make_expert_outputs(max(T * min(k, R), 1), H, seed=seed + 1)
+    got_r = host_bits(h.combine_ranks(dev_bf16(part)))
+    want_r, mag_r = oracle.combine_ranks(part, rl["rank_pos"], return_magnitude=True)
+    assert_combine_close(got_r, want_r, mag_r, R)
+    # decode-time path (token limit 1024)
+    if T <= 1024:
+        out = h.ll_dispatch(dev_i32(idx), dx, C)
+        v = h.ll_view()
+        fc = oracle.layout_fixed_capacity(idx, E, C)
+        assert np.array_equal(v["pos"].cpu().numpy().astype(np.int64), fc["pos"])
+        assert np.array_equal(v["counts"].cpu().numpy(), fc["counts"])
+        mapped = fc["pos"][fc["pos"] >= 0]
+        want_ll = oracle.dispatch_bf16(x, fc["pos"], rows=E * C)
+        assert np.array_equal(host_bits(out)[mapped], want_ll[mapped])
+        yl = make_expert_outputs(E * C, H, seed=seed + 2)
+        got_l = host_bits(h.ll_combine(dev_bf16(yl), dev_f32(w)))
+        want_l, mag_l = oracle.combine(yl, w, fc["pos"], return_magnitude=True)
+        assert_combine_close(got_l, want_l, mag_l, k)
