@@ -93,16 +93,20 @@ def moe_layout_view(h: int) -> MoeLayoutView:
     return v
 
 
-def moe_dispatch(h: int, x: torch.Tensor, dtype: int, out: torch.Tensor,
-                 scales: torch.Tensor | None = None, stream=None) -> None:
+def _payload_ptrs(x, dtype, out, scales):
     px = _ptr(x, torch.bfloat16, "x")
-    want = torch.bfloat16 if dtype == MOE_DTYPE_BF16 else torch.uint8
-    po = _ptr(out, want, "out")
+    po = _ptr(out, torch.bfloat16 if dtype == MOE_DTYPE_BF16 else torch.uint8, "out")
     ps = None
     if dtype == MOE_DTYPE_FP8_E4M3:
         ps = _ptr(scales, torch.float32, "scales")
     elif dtype == MOE_DTYPE_MXFP8_E4M3:
         ps = _ptr(scales, torch.uint8, "scales")
+    return px, po, ps
+
+
+def moe_dispatch(h: int, x: torch.Tensor, dtype: int, out: torch.Tensor,
+                 scales: torch.Tensor | None = None, stream=None) -> None:
+    px, po, ps = _payload_ptrs(x, dtype, out, scales)
     _lib.check(_lib.load().moe_dispatch(ctypes.c_void_p(h), ctypes.c_void_p(px), int(dtype),
                                         ctypes.c_void_p(po), ctypes.c_void_p(ps),
                                         out.shape[0], _stream(stream, x.device)))
@@ -160,17 +164,6 @@ def moe_route(h: int, logits: torch.Tensor, score: int, topk_idx: torch.Tensor,
     _lib.check(_lib.load().moe_route(ctypes.c_void_p(h), ctypes.c_void_p(pl), int(logits.shape[0]),
                                      int(score), ctypes.c_void_p(pi), ctypes.c_void_p(pw),
                                      _stream(stream, logits.device)))
-
-
-def _payload_ptrs(x, dtype, out, scales):
-    px = _ptr(x, torch.bfloat16, "x")
-    po = _ptr(out, torch.bfloat16 if dtype == MOE_DTYPE_BF16 else torch.uint8, "out")
-    ps = None
-    if dtype == MOE_DTYPE_FP8_E4M3:
-        ps = _ptr(scales, torch.float32, "scales")
-    elif dtype == MOE_DTYPE_MXFP8_E4M3:
-        ps = _ptr(scales, torch.uint8, "scales")
-    return px, po, ps
 
 
 def moe_ll_dispatch(h: int, topk_idx: torch.Tensor, capacity: int, x: torch.Tensor, dtype: int,

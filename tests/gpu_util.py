@@ -3,7 +3,6 @@ the oracle comparisons."""
 import numpy as np
 import torch
 
-import oracle
 from conftest import combine_tolerance
 
 
@@ -58,10 +57,6 @@ def assert_combine_close(got_bits, ref_bits, mag, k, extra=None):
     big = np.abs(ref) >= 1e-2
     rel = np.abs(got - ref)[big] / np.abs(ref)[big] if big.any() else np.zeros(1)
     return float(rel.max()), float(np.mean(got_bits == ref_bits))
-
-
-def oracle_layout(idx, E, R):
-    return oracle.layout(idx, E, R)
 
 
 def router_weight_tol(logits, idx, w_ref):
