@@ -212,3 +212,15 @@ def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(2) == b"MOE_ERR_UNSUPPORTED"
     assert lib.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/moe_ep.h is usable from plain C: the round-trip program compiles
+    with gcc -x c -Werror and links against the library (run on the GPU)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "moe_c_abi_build", os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    out = mod.build(str(tmp_path / "abi_roundtrip"))
+    assert os.path.exists(out)
