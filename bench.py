@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--buffer-sets", type=int, default=3,
                     help="input/output buffer sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--instrument-every", type=int, default=5,
+                    help="record per-op HIP events in every N-th timed step (1: every step)")
     ap.add_argument("--skip", default="",
                     help="comma list of report sections to leave out: rank, decode (router and "
                          "decode-time path), sweep")
@@ -181,20 +183,29 @@ def main():
             run_op(name)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps. HIP events on the launch stream mark every
-    # op boundary (one event between consecutive ops, so op i spans events i
-    # and i+1 of its step); each event costs a few microseconds of GPU time,
-    # which the step time includes.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
-          for _ in range(args.steps)]
+    # Timed region: exactly K steps. Every `instrument_every`-th step (and the
+    # first) records HIP events on the launch stream at every op boundary (op i
+    # spans events i and i+1 of that step); the per-op times and the roofline
+    # come from those steps. Each event costs about 3 us of GPU time, so the
+    # other steps run without events and the wall time per step is not
+    # inflated by the timing itself.
+    every = max(1, args.instrument_every)
+    instrumented = [i for i in range(args.steps) if i % every == 0]
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+          for i in instrumented}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         cur["i"] = i % len(sets)
-        ev[i][0].record(stream)
+        marks = ev.get(i)
+        if marks is None:
+            for name in ops:
+                run_op(name)
+            continue
+        marks[0].record(stream)
         for j, name in enumerate(ops):
             run_op(name)
-            ev[i][j + 1].record(stream)
+            marks[j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -203,7 +214,7 @@ def main():
     step_bytes = sum(nbytes.values())
     per_op = {}
     for j, name in enumerate(ops):
-        us = np.array([ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(args.steps)])
+        us = np.array([ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in instrumented])
         per_op[name] = {"bytes": nbytes[name], "us_mean": round(float(us.mean()), 2),
                         "us_median": round(float(np.median(us)), 2),
                         "GBps": round(nbytes[name] / (us.mean() * 1e-6) / 1e9, 1),
@@ -434,6 +445,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant)},
         "ops": per_op,
+        "instrumented_steps": len(instrumented),
         "sustained": sustained,
         "workgroup_sweep_GBps": sweep,
         "rank_exchange": exchange,
