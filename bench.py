@@ -119,12 +119,12 @@ def main():
                     help="record per-op HIP events in every N-th timed step (1: every step)")
     ap.add_argument("--skip", default="",
                     help="comma list of report sections to leave out: rank, decode (router and "
-                         "decode-time path), sweep")
+                         "decode-time path), sweep, others (the other full-size workloads)")
     args = ap.parse_args()
 
     skip = {x for x in args.skip.split(",") if x}
-    if not skip <= {"rank", "decode", "sweep"}:
-        ap.error(f"--skip takes rank, decode, sweep; got {args.skip}")
+    if not skip <= {"rank", "decode", "sweep", "others"}:
+        ap.error(f"--skip takes rank, decode, sweep, others; got {args.skip}")
     if "sweep" in skip:
         args.workgroup_sweep = 0
     if args.gpus != 1:
@@ -421,6 +421,41 @@ def main():
         decode["step_graph_us"] = sustained_us(lambda i: graph.replay(), args.sustained_iters)
         del graph, dsets, hd
 
+    # The other full-size workloads (not the headline): sustained per-op
+    # rates, 3 rotating buffer sets each, routing by the router kernel.
+    others = {}
+    if args.sustained_iters > 0 and "others" not in skip:
+        for name in ("deepseek16b", "qwen3_skewed"):
+            wo = make_workload(name)
+            so = wo.shape
+            To, Ho, ko = so.tokens, so.hidden, so.topk
+            ho = Handle(To, Ho, ko, so.experts, so.ranks, device=dev)
+            oi, ow = ho.route(torch.from_numpy(wo.logits).to(dev), so.weights)
+            xo = torch.from_numpy(wo.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+            So = To * ko
+            osets = [{"idx": oi.clone(), "w": ow.clone(), "x": xo.clone(),
+                      "d": torch.empty((So, Ho), dtype=torch.bfloat16, device=dev),
+                      "q": torch.empty((So, Ho), dtype=torch.uint8, device=dev),
+                      "qs": torch.empty((So, Ho // 128), dtype=torch.float32, device=dev),
+                      "c": torch.empty((To, Ho), dtype=torch.bfloat16, device=dev)} for _ in range(3)]
+            del xo
+            O = lambda i: osets[i % 3]   # noqa: E731
+            ob = op_bytes(To, Ho, ko)
+            calls = {"layout": lambda i: ho.layout(O(i)["idx"]),
+                     "dispatch_bf16": lambda i: ho.dispatch(O(i)["x"], out=O(i)["d"]),
+                     "dispatch_fp8": lambda i: ho.dispatch(O(i)["x"], fp8=True, out=O(i)["q"],
+                                                           scales=O(i)["qs"]),
+                     "combine": lambda i: ho.combine(O(i)["d"], O(i)["w"], out=O(i)["c"])}
+            for i in range(3):                    # lay out every set once before timing combine
+                ho.layout(O(i)["idx"])
+            row = {"tokens": To, "hidden": Ho, "experts": so.experts, "topk": ko}
+            for op, fn in calls.items():
+                us = sustained_us(fn, args.sustained_iters)
+                row[op] = {"us_median": us, "GBps": round(ob[op] / (us * 1e-6) / 1e9, 1)}
+            others[name] = row
+            del osets, ho
+        torch.cuda.synchronize()
+
     dominant = max(("dispatch_bf16", "dispatch_fp8", "combine"), key=lambda n: per_op[n]["us_mean"])
     achieved = per_op[dominant]["GBps"]
     result = {
@@ -451,6 +486,7 @@ def main():
         "rank_exchange": exchange,
         "router": router,
         "decode": decode,
+        "other_workloads": others,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_tokens)
