@@ -166,6 +166,12 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
 
   for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) s_cur[i] = 0;
 
+  // This wavefront's slot ids, loaded first so that their latency overlaps
+  // the histogram reads below.
+  const int base = blockIdx.x * kLayoutChunk + wave * (kLayoutSteps * 64);
+  int ids[kLayoutSteps];
+  load_buckets<kRanks>(b, base, lane, ids);
+
   // Column sums of the per-workgroup histograms: the bucket totals, and the
   // part that earlier workgroups (earlier slots) contribute.
   for (int e = tid; e < E; e += kLayoutThreads) {
@@ -182,10 +188,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
   __syncthreads();
 
   // Pass 1 over this workgroup's chunk: per-wavefront histograms.
-  const int base = blockIdx.x * kLayoutChunk + wave * (kLayoutSteps * 64);
-  int ids[kLayoutSteps];
   uint64_t peers[kLayoutSteps];
-  load_buckets<kRanks>(b, base, lane, ids);
   int32_t* my_cur = s_cur + wave * E;
 #pragma unroll
   for (int s = 0; s < kLayoutSteps; ++s) {
