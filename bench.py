@@ -421,6 +421,26 @@ def main():
         decode["step_graph_us"] = sustained_us(lambda i: graph.replay(), args.sustained_iters)
         del graph, dsets, hd
 
+        # Decode-time dispatch against layout + dispatch over batch sizes (bf16,
+        # capacity = T, so nothing is dropped).
+        scaling = {}
+        for Tn in (32, 128, 512, 1024):
+            hn = Handle(Tn, H, k, E, R, device=dev)
+            ni, _ = hn.route(logits[:Tn].contiguous(), s.weights)
+            nx = sets[0]["x"][:Tn].contiguous()
+            n_ll = torch.empty((E * Tn, H), dtype=torch.bfloat16, device=dev)
+            n_std = torch.empty((Tn * k, H), dtype=torch.bfloat16, device=dev)
+
+            def n_standard(i):
+                hn.layout(ni)
+                hn.dispatch(nx, out=n_std)
+            scaling[str(Tn)] = {
+                "ll_dispatch_bf16_us": sustained_us(lambda i: hn.ll_dispatch(ni, nx, Tn, out=n_ll),
+                                                    args.sustained_iters),
+                "layout_plus_dispatch_bf16_us": sustained_us(n_standard, args.sustained_iters)}
+            del hn, n_ll, n_std
+        decode["by_tokens"] = scaling
+
     # The other full-size workloads (not the headline): sustained per-op
     # rates, 3 rotating buffer sets each, routing by the router kernel.
     others = {}

@@ -41,12 +41,16 @@
 // that does not depend on the routing. Here expert e owns rows
 // [e*C, (e+1)*C); a slot's row is e*C plus its stable rank among the slots
 // routed to e (token order, then slot order), and slots ranked C or more are
-// dropped. Each wavefront computes the ranks of its own token's slots by
-// counting matching ids among all earlier slots (one coalesced load and one
-// ballot per 64 slots and slot), so no workgroup waits for another; the last
-// workgroup of the grid builds the per-expert histogram in LDS and publishes
-// counts and status. The counting costs O(T*k) per wavefront, which is why
-// this path is limited to small batches (MOE_EP_LL_MAX_TOKENS).
+// dropped. A workgroup takes one token and four of its column slices, one per
+// wavefront. A slot's rank is the number of matching ids among the earlier
+// slots: below kFixedSharedFrom tokens each wavefront counts them itself (no
+// barrier at all); from there on the four wavefronts split the count and add
+// their shares through LDS. The last workgroup of the grid builds the
+// per-expert histogram in LDS and publishes counts and status. No workgroup
+// waits for another. The counting is O(T*k) per workgroup, which is why this
+// path is limited to small batches (MOE_EP_LL_MAX_TOKENS).
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -78,55 +82,347 @@ __device__ __forceinline__ void store_row(u32x4* dst, const u32x4& v) {
   __builtin_nontemporal_store(v, dst);
 }
 
-// Where a payload kernel finds the destination rows of token t's slots.
-// rows_of fills p[] for slots j0 .. j0+kSlotBatch-1 (-1: no row); `record`
-// is true for exactly one wavefront per token (its first column slice).
+// Where a payload function finds the destination rows of token t's slots:
+// rows_of fills p[] for slots j0 .. j0+kSlotBatch-1 (-1: no row).
 
 // Standard layout: the table pos[T, k] written by the layout kernels.
 struct TableRows {
-  static constexpr bool kCountsBlock = false;
   const int32_t* pos;
   int topk;
   int64_t rows;
-  __device__ __forceinline__ void rows_of(int t, int j0, bool, int (&p)[kSlotBatch]) const {
+  __device__ __forceinline__ void rows_of(int t, int j0, int (&p)[kSlotBatch]) const {
     load_rows(pos + static_cast<size_t>(t) * topk, j0, topk, rows, p);
   }
-  __device__ void counts_block(int) const {}
 };
 
-// Fixed-capacity layout, computed on the fly (decode-time dispatch).
+// Decode-time layout: the token's rows, computed by its workgroup into LDS.
+struct SharedRows {
+  const int32_t* s_pos;   // [topk] in LDS
+  int topk;
+  __device__ __forceinline__ void rows_of(int, int j0, int (&p)[kSlotBatch]) const {
+#pragma unroll
+    for (int jj = 0; jj < kSlotBatch; ++jj) p[jj] = j0 + jj < topk ? s_pos[j0 + jj] : -1;
+  }
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Four fp32 values -> four E4M3 codes packed little-endian in one dword.
+__device__ __forceinline__ uint32_t pack_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// FP8 E4M3 quantisation of one lane's 16 channels (unit u of the row at src;
+// 8 consecutive lanes form a 128-channel block): codes q and the block scale.
+__device__ __forceinline__ void quantize_fp8(const u32x4* __restrict__ src, int u, bool active,
+                                             u32x4& q, float& scale) {
+  u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+  if (active) {
+    a = src[2 * u];
+    b = src[2 * u + 1];
+  }
+  float f[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
+                 bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
+                 bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
+                 bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(f[i]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  m = fmaxf(m, __shfl_xor(m, 4, 64));
+  scale = m / 448.0f;
+  if (m > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[i] = __builtin_amdgcn_fmed3f(f[i] / scale, -448.0f, 448.0f);
+  }
+  q.x = pack_e4m3(f[0], f[1], f[2], f[3]);
+  q.y = pack_e4m3(f[4], f[5], f[6], f[7]);
+  q.z = pack_e4m3(f[8], f[9], f[10], f[11]);
+  q.w = pack_e4m3(f[12], f[13], f[14], f[15]);
+}
+
+// MXFP8 quantisation of one lane's 16 channels (a lane pair is one 32-channel
+// block): codes q and, in lanes 8i, the dword of four E8M0 codes of blocks
+// u/2 .. u/2+3.
+__device__ __forceinline__ void quantize_mxfp8(const u32x4* __restrict__ src, int u, int lane,
+                                               bool active, u32x4& q, uint32_t& word) {
+  u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+  if (active) {
+    a = src[2 * u];
+    b = src[2 * u + 1];
+  }
+  float f[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
+                 bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
+                 bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
+                 bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(f[i]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  const uint32_t mb = __float_as_uint(m);
+  int shared = -127;
+  if (mb != 0u) {
+    const int fl = mb >= 0x00800000u ? static_cast<int>(mb >> 23) - 127   // normal
+                                     : 31 - __clz(mb) - 149;                // subnormal
+    shared = fl - 8 < -127 ? -127 : (fl - 8 > 127 ? 127 : fl - 8);
+  }
+  const float inv = __uint_as_float(static_cast<uint32_t>(127 - shared) << 23);   // 2^-shared
+#pragma unroll
+  for (int i = 0; i < 16; ++i) f[i] = __builtin_amdgcn_fmed3f(f[i] * inv, -448.0f, 448.0f);
+  q.x = pack_e4m3(f[0], f[1], f[2], f[3]);
+  q.y = pack_e4m3(f[4], f[5], f[6], f[7]);
+  q.z = pack_e4m3(f[8], f[9], f[10], f[11]);
+  q.w = pack_e4m3(f[12], f[13], f[14], f[15]);
+  // Lane 8i gathers the codes of blocks u/2 .. u/2+3 (lanes 8i, 8i+2, 8i+4, 8i+6).
+  const uint32_t code = static_cast<uint32_t>(shared + 127);
+  const uint32_t c1 = __shfl(code, lane + 2, 64);
+  const uint32_t c2 = __shfl(code, lane + 4, 64);
+  const uint32_t c3 = __shfl(code, lane + 6, 64);
+  word = code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+}
+
+// Payload of one (token t, column slice) work item for each dtype; `rows`
+// supplies the destination rows. A lane moves 16 bytes per access.
+
+// bf16: a 512-channel slice (8 channels per lane), read once, stored to every row.
+template <class Rows>
+__device__ __forceinline__ void bf16_item(const u32x4* __restrict__ x, const Rows& rows,
+                                          u32x4* __restrict__ out, int t, int slice, int nvec,
+                                          int topk) {
+  const int lane = threadIdx.x & 63;
+  const int v = slice * 64 + lane;
+  const bool active = v < nvec;
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if (active) r = x[static_cast<size_t>(t) * nvec + v];
+  for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
+    int p[kSlotBatch];
+    rows.rows_of(t, j0, p);
+#pragma unroll
+    for (int jj = 0; jj < kSlotBatch; ++jj)
+      if (p[jj] >= 0 && active) store_row(&out[static_cast<size_t>(p[jj]) * nvec + v], r);
+  }
+}
+
+// FP8 E4M3 with one fp32 scale per 128 channels: a 1024-channel slice.
+template <class Rows>
+__device__ __forceinline__ void fp8_item(const u32x4* __restrict__ x, const Rows& rows,
+                                         u32x4* __restrict__ out, float* __restrict__ scales,
+                                         int t, int slice, int hidden, int topk) {
+  const int lane = threadIdx.x & 63;
+  const int units = hidden >> 4;    // 16 channels per lane
+  const int nscale = hidden >> 7;   // one scale per 128 channels
+  const int u = slice * 64 + lane;
+  // units is a multiple of 8, so each 8-lane group is wholly active or not.
+  const bool active = u < units;
+  u32x4 q;
+  float scale;
+  quantize_fp8(x + static_cast<size_t>(t) * (hidden >> 3), u, active, q, scale);
+  const bool scale_lane = active && (lane & 7) == 0;
+  for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
+    int p[kSlotBatch];
+    rows.rows_of(t, j0, p);
+#pragma unroll
+    for (int jj = 0; jj < kSlotBatch; ++jj) {
+      if (p[jj] < 0) continue;
+      if (active) store_row(&out[static_cast<size_t>(p[jj]) * units + u], q);
+      if (scale_lane) scales[static_cast<size_t>(p[jj]) * nscale + (u >> 3)] = scale;
+    }
+  }
+}
+
+// MXFP8 (OCP Microscaling v1.0, E4M3 elements): 32-channel blocks share an
+// E8M0 power-of-two scale. A lane holds 16 channels, so a block is a lane
+// pair; shared = floor(log2 amax) - 8 (8: exponent of E4M3's largest normal),
+// clamped to E8M0's [-127, 127], read off amax's fp32 bit fields. Elements are
+// x * 2^-shared (exact: a power of two, and every product that can round to a
+// nonzero code is a normal fp32), clamped to +-448 and converted by the
+// hardware fp32 -> fp8 instruction (round-to-nearest-even). An all-zero block
+// gets code 0 and signed-zero elements. Four E8M0 bytes go out per dword
+// store. The Hybrid-EP news item ("Efficiency Numbers") reports its Qwen3 run
+// in MXFP8.
+template <class Rows>
+__device__ __forceinline__ void mxfp8_item(const u32x4* __restrict__ x, const Rows& rows,
+                                           u32x4* __restrict__ out, uint32_t* __restrict__ scales,
+                                           int t, int slice, int hidden, int topk) {
+  const int lane = threadIdx.x & 63;
+  const int units = hidden >> 4;           // 16 channels per lane
+  const int scale_words = hidden >> 7;     // 4 one-byte scales per dword, per row
+  const int u = slice * 64 + lane;
+  // units is a multiple of 8, so each 8-lane group is wholly active or not.
+  const bool active = u < units;
+  u32x4 q;
+  uint32_t word;
+  quantize_mxfp8(x + static_cast<size_t>(t) * (hidden >> 3), u, lane, active, q, word);
+  const bool scale_lane = active && (lane & 7) == 0;
+  for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
+    int p[kSlotBatch];
+    rows.rows_of(t, j0, p);
+#pragma unroll
+    for (int jj = 0; jj < kSlotBatch; ++jj) {
+      if (p[jj] < 0) continue;
+      if (active) store_row(&out[static_cast<size_t>(p[jj]) * units + u], q);
+      if (scale_lane) scales[static_cast<size_t>(p[jj]) * scale_words + (u >> 3)] = word;
+    }
+  }
+}
+
+// Channels per lane and slices per token of each dtype.
+__host__ __device__ constexpr int lane_channels(int dtype) {
+  return dtype == MOE_DTYPE_BF16 ? 8 : 16;
+}
+
+// The scale pointer of each dtype (fp32 per 128 channels, or four E8M0 bytes
+// per dword); the kernels take it typed and restrict-qualified, so that the
+// compiler knows scale stores never alias the row indices it loads.
+template <int kDtype>
+using ScalePtr = typename std::conditional<kDtype == MOE_DTYPE_MXFP8_E4M3, uint32_t, float>::type*;
+
+template <int kDtype, class Rows>
+__device__ __forceinline__ void payload_item(const u32x4* __restrict__ x, const Rows& rows,
+                                             u32x4* __restrict__ out,
+                                             ScalePtr<kDtype> __restrict__ scales, int t,
+                                             int slice, int hidden, int topk) {
+  if constexpr (kDtype == MOE_DTYPE_BF16)
+    bf16_item(x, rows, out, t, slice, hidden >> 3, topk);
+  else if constexpr (kDtype == MOE_DTYPE_FP8_E4M3)
+    fp8_item(x, rows, out, scales, t, slice, hidden, topk);
+  else
+    mxfp8_item(x, rows, out, scales, t, slice, hidden, topk);
+}
+
+// Standard dispatch: every wavefront is one independent (token, slice) item;
+// workgroups [0, payload_blocks) loop over the items. The bodies are written
+// out per dtype (rather than through the payload functions above, which the
+// decode-time kernel uses): with them written out, hipcc keeps the
+// contiguous-batch fast path for the row indices, worth 1-2.5% here.
+template <class Rows>
+__global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_kernel(
+    const u32x4* __restrict__ x, Rows src_rows, u32x4* __restrict__ out, int num_tokens,
+    int nvec, int slices, int payload_blocks) {
+  const int lane = threadIdx.x & 63;
+  const int nitems = num_tokens * slices;
+  const int topk = src_rows.topk;
+  for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
+       item += payload_blocks * kItemWaves) {
+    const int t = item / slices;
+    const int slice = item - t * slices;
+    const int v = slice * 64 + lane;
+    const bool active = v < nvec;
+    u32x4 r = {0u, 0u, 0u, 0u};
+    if (active) r = x[static_cast<size_t>(t) * nvec + v];
+    for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
+      int p[kSlotBatch];
+      src_rows.rows_of(t, j0, p);
+#pragma unroll
+      for (int jj = 0; jj < kSlotBatch; ++jj)
+        if (p[jj] >= 0 && active) store_row(&out[static_cast<size_t>(p[jj]) * nvec + v], r);
+    }
+  }
+}
+
+template <class Rows>
+__global__ __launch_bounds__(64 * kItemWaves) void dispatch_fp8_kernel(
+    const u32x4* __restrict__ x, Rows src_rows, u32x4* __restrict__ out,
+    float* __restrict__ scales, int num_tokens, int hidden, int slices, int payload_blocks) {
+  const int lane = threadIdx.x & 63;
+  const int units = hidden >> 4;    // 16 channels per lane
+  const int nscale = hidden >> 7;   // one scale per 128 channels
+  const int nitems = num_tokens * slices;
+  const int topk = src_rows.topk;
+  for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
+       item += payload_blocks * kItemWaves) {
+    const int t = item / slices;
+    const int slice = item - t * slices;
+    const int u = slice * 64 + lane;
+    // units is a multiple of 8, so each 8-lane group is wholly active or not.
+    const bool active = u < units;
+    u32x4 q;
+    float scale;
+    quantize_fp8(x + static_cast<size_t>(t) * (hidden >> 3), u, active, q, scale);
+    const bool scale_lane = active && (lane & 7) == 0;
+    for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
+      int p[kSlotBatch];
+      src_rows.rows_of(t, j0, p);
+#pragma unroll
+      for (int jj = 0; jj < kSlotBatch; ++jj) {
+        if (p[jj] < 0) continue;
+        if (active) store_row(&out[static_cast<size_t>(p[jj]) * units + u], q);
+        if (scale_lane) scales[static_cast<size_t>(p[jj]) * nscale + (u >> 3)] = scale;
+      }
+    }
+  }
+}
+
+template <class Rows>
+__global__ __launch_bounds__(64 * kItemWaves) void dispatch_mxfp8_kernel(
+    const u32x4* __restrict__ x, Rows src_rows, u32x4* __restrict__ out,
+    uint32_t* __restrict__ scales, int num_tokens, int hidden, int slices, int payload_blocks) {
+  const int lane = threadIdx.x & 63;
+  const int units = hidden >> 4;           // 16 channels per lane
+  const int scale_words = hidden >> 7;     // 4 one-byte scales per dword, per row
+  const int nitems = num_tokens * slices;
+  const int topk = src_rows.topk;
+  for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
+       item += payload_blocks * kItemWaves) {
+    const int t = item / slices;
+    const int slice = item - t * slices;
+    const int u = slice * 64 + lane;
+    // units is a multiple of 8, so each 8-lane group is wholly active or not.
+    const bool active = u < units;
+    u32x4 q;
+    uint32_t word;
+    quantize_mxfp8(x + static_cast<size_t>(t) * (hidden >> 3), u, lane, active, q, word);
+    const bool scale_lane = active && (lane & 7) == 0;
+    for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
+      int p[kSlotBatch];
+      src_rows.rows_of(t, j0, p);
+#pragma unroll
+      for (int jj = 0; jj < kSlotBatch; ++jj) {
+        if (p[jj] < 0) continue;
+        if (active) store_row(&out[static_cast<size_t>(p[jj]) * units + u], q);
+        if (scale_lane) scales[static_cast<size_t>(p[jj]) * scale_words + (u >> 3)] = word;
+      }
+    }
+  }
+}
+
+// Decode-time (fixed-capacity) layout: expert e owns rows [e*C, (e+1)*C); a
+// slot's row is e*C plus its rank among the slots routed to e in (token,
+// slot) order, or -1 from rank C on (dropped).
 constexpr int kRankLoads = 16;
 constexpr int kCountLoads = 8;
-struct FixedCapacityRows {
-  static constexpr bool kCountsBlock = true;
+constexpr int kFixedWaves = 4;   // wavefronts (column slices) per decode-time workgroup
+constexpr int kFixedSharedFrom = 256;   // tokens from which a workgroup shares the rank count
+
+struct FixedCapacity {
   const int32_t* idx;   // [T, k] expert ids
   int topk, num_experts, capacity;
   int32_t* pos;         // [T, k] rows, recorded for combine
   int32_t* counts;      // [E] rows received per expert
   int32_t* status;      // [4] invalid, placed, T, dropped
 
-  __device__ __forceinline__ void rows_of(int t, int j0, bool record, int (&p)[kSlotBatch]) const {
+  // Per-lane match counts for slots j0 .. j0+kSlotBatch-1 of token t (ids e[]):
+  // matches among the earlier tokens' slots [0, t*k) in chunks of 64 ids
+  // strided by `waves` wavefronts starting at chunk `wave` (kRankLoads chunks
+  // in flight), plus, for wavefront 0, the token's own earlier slots (`own`:
+  // this token's id of slot `lane`). One compare and one add per id and slot.
+  __device__ __forceinline__ void count_batch(int t, int j0, int wave, int waves, int own,
+                                              const int (&e)[kSlotBatch],
+                                              uint32_t (&cnt)[kSlotBatch]) const {
     const int base = t * topk;
-    int e[kSlotBatch], rank[kSlotBatch];
-#pragma unroll
-    for (int jj = 0; jj < kSlotBatch; ++jj) {
-      e[jj] = idx[base + (j0 + jj < topk ? j0 + jj : topk - 1)];
-      rank[jj] = 0;
-    }
-    // Rank of slot (t, j) = number of earlier slots with the same id: the
-    // slots of earlier tokens, [0, base), plus slots j' < j of this token.
-    // Each lane counts matches in its registers (one compare and one add per
-    // id and slot; kRankLoads chunks of 64 ids in flight), then one wavefront
-    // sum per slot.
     const int lane = threadIdx.x & 63;
-    uint32_t cnt[kSlotBatch];
 #pragma unroll
     for (int jj = 0; jj < kSlotBatch; ++jj) cnt[jj] = 0u;
-    for (int c = 0; c < base; c += 64 * kRankLoads) {
+    const int stride = waves * 64;
+    for (int c = wave * 64; c < base; c += stride * kRankLoads) {
       int id[kRankLoads];
 #pragma unroll
       for (int q = 0; q < kRankLoads; ++q) {
-        const int s = c + q * 64 + lane;
+        const int s = c + q * stride + lane;
         id[q] = idx[s < base ? s : 0];
         if (s >= base) id[q] = -1;
       }
@@ -135,21 +431,44 @@ struct FixedCapacityRows {
 #pragma unroll
         for (int jj = 0; jj < kSlotBatch; ++jj) cnt[jj] += id[q] == e[jj] ? 1u : 0u;
     }
-    const int own = idx[base + (lane < topk ? lane : 0)];   // this token's ids, lanes < topk
+    if (wave == 0) {
 #pragma unroll
-    for (int jj = 0; jj < kSlotBatch; ++jj) {
-      cnt[jj] += (lane < j0 + jj && own == e[jj]) ? 1u : 0u;
-      rank[jj] = static_cast<int>(wave_sum_u32(cnt[jj]));
+      for (int jj = 0; jj < kSlotBatch; ++jj)
+        cnt[jj] += (lane < j0 + jj && own == e[jj]) ? 1u : 0u;
     }
-    int mine = -1;
+  }
+
+  __device__ __forceinline__ void batch_ids(int t, int j0, int (&e)[kSlotBatch]) const {
+    const int base = t * topk;
 #pragma unroll
-    for (int jj = 0; jj < kSlotBatch; ++jj) {
-      const bool ok = j0 + jj < topk && static_cast<unsigned>(e[jj]) <
-                      static_cast<unsigned>(num_experts) && rank[jj] < capacity;
-      p[jj] = ok ? e[jj] * capacity + rank[jj] : -1;
-      if (lane == jj) mine = p[jj];
+    for (int jj = 0; jj < kSlotBatch; ++jj)
+      e[jj] = idx[base + (j0 + jj < topk ? j0 + jj : topk - 1)];
+  }
+
+  __device__ __forceinline__ int row_of(int e, int rank) const {
+    return static_cast<unsigned>(e) < static_cast<unsigned>(num_experts) && rank < capacity
+               ? e * capacity + rank
+               : -1;
+  }
+
+  // This wavefront's share of the ranks of token t's slots (one of `waves`),
+  // summed over its lanes into part[slot]. Returns this token's id of slot
+  // `lane` (lanes < topk).
+  __device__ __forceinline__ int rank_share(int t, int wave, int waves, int32_t* part) const {
+    const int lane = threadIdx.x & 63;
+    const int own = idx[t * topk + (lane < topk ? lane : 0)];
+    for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
+      int e[kSlotBatch];
+      uint32_t cnt[kSlotBatch];
+      batch_ids(t, j0, e);
+      count_batch(t, j0, wave, waves, own, e, cnt);
+#pragma unroll
+      for (int jj = 0; jj < kSlotBatch; ++jj) {
+        const uint32_t sum = wave_sum_u32(cnt[jj]);
+        if (lane == 0 && j0 + jj < topk) part[j0 + jj] = static_cast<int32_t>(sum);
+      }
     }
-    if (record && lane < kSlotBatch && j0 + lane < topk) pos[base + j0 + lane] = mine;
+    return own;
   }
 
   // Run by the grid's last workgroup: histogram of all slots in LDS, then
@@ -200,190 +519,80 @@ struct FixedCapacityRows {
   }
 };
 
-// Payload kernels. Workgroups [0, payload_blocks) run the (token, slice)
-// items; with a FixedCapacityRows source one more workgroup follows and
-// publishes the counts.
-template <class Rows>
-__global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_kernel(
-    const u32x4* __restrict__ x, Rows src_rows, u32x4* __restrict__ out, int num_tokens,
-    int nvec, int slices, int payload_blocks) {
-  if constexpr (Rows::kCountsBlock) {
-    if (static_cast<int>(blockIdx.x) == payload_blocks) {
-      src_rows.counts_block(num_tokens);
-      return;
-    }
-  }
-  const int lane = threadIdx.x & 63;
-  const int nitems = num_tokens * slices;
-  const int topk = src_rows.topk;
-  for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
-       item += payload_blocks * kItemWaves) {
-    const int t = item / slices;
-    const int slice = item - t * slices;
-    const int v = slice * 64 + lane;
-    const bool active = v < nvec;
-    u32x4 r = {0u, 0u, 0u, 0u};
-    if (active) r = x[static_cast<size_t>(t) * nvec + v];
-    for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
-      int p[kSlotBatch];
-      src_rows.rows_of(t, j0, slice == 0, p);
+// Decode-time rows computed by one wavefront alone (small batches): the whole
+// count of earlier matching ids, no LDS and no barrier. `record` makes it
+// store the token's rows for combine (one wavefront per token does).
+struct WaveRows {
+  FixedCapacity fc;
+  bool record;
+  __device__ __forceinline__ void rows_of(int t, int j0, int (&p)[kSlotBatch]) const {
+    const int lane = threadIdx.x & 63;
+    const int topk = fc.topk;
+    const int own = fc.idx[t * topk + (lane < topk ? lane : 0)];
+    int e[kSlotBatch];
+    uint32_t cnt[kSlotBatch];
+    fc.batch_ids(t, j0, e);
+    fc.count_batch(t, j0, 0, 1, own, e, cnt);
+    int mine = -1;
 #pragma unroll
-      for (int jj = 0; jj < kSlotBatch; ++jj)
-        if (p[jj] >= 0 && active) store_row(&out[static_cast<size_t>(p[jj]) * nvec + v], r);
+    for (int jj = 0; jj < kSlotBatch; ++jj) {
+      const int rank = static_cast<int>(wave_sum_u32(cnt[jj]));
+      p[jj] = j0 + jj < topk ? fc.row_of(e[jj], rank) : -1;
+      if (lane == jj) mine = p[jj];
     }
+    if (record && lane < kSlotBatch && j0 + lane < topk) fc.pos[t * topk + j0 + lane] = mine;
   }
-}
+};
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Four fp32 values -> four E4M3 codes packed little-endian in one dword.
-__device__ __forceinline__ uint32_t pack_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return static_cast<uint32_t>(w);
-}
-
-template <class Rows>
-__global__ __launch_bounds__(64 * kItemWaves) void dispatch_fp8_kernel(
-    const u32x4* __restrict__ x, Rows src_rows, u32x4* __restrict__ out,
-    float* __restrict__ scales, int num_tokens, int hidden, int slices, int payload_blocks) {
-  if constexpr (Rows::kCountsBlock) {
-    if (static_cast<int>(blockIdx.x) == payload_blocks) {
-      src_rows.counts_block(num_tokens);
-      return;
-    }
+// Decode-time dispatch: a workgroup of kFixedWaves wavefronts takes one
+// (token, group of kFixedWaves column slices) item, looping over items when
+// the grid is capped. Its wavefronts split the token's rank count, add their
+// shares through LDS, and then each moves one slice; the group holding slice
+// 0 records the token's rows. The grid's last workgroup publishes the counts.
+// No workgroup waits for another.
+template <int kDtype, bool kShared>
+__global__ __launch_bounds__(64 * kFixedWaves) void dispatch_fixed_kernel(
+    const u32x4* __restrict__ x, FixedCapacity fc, u32x4* __restrict__ out,
+    ScalePtr<kDtype> __restrict__ scales, int num_tokens, int hidden, int slices, int groups,
+    int work_blocks) {
+  __shared__ int32_t s_part[kFixedWaves][MOE_EP_MAX_TOPK];
+  __shared__ int32_t s_pos[MOE_EP_MAX_TOPK];
+  if (static_cast<int>(blockIdx.x) == work_blocks) {
+    fc.counts_block(num_tokens);
+    return;
   }
-  const int lane = threadIdx.x & 63;
-  const int units = hidden >> 4;    // 16 channels per lane
-  const int nscale = hidden >> 7;   // one scale per 128 channels
-  const int nitems = num_tokens * slices;
-  const int topk = src_rows.topk;
-  for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
-       item += payload_blocks * kItemWaves) {
-    const int t = item / slices;
-    const int slice = item - t * slices;
-    const int u = slice * 64 + lane;
-    // units is a multiple of 8, so each 8-lane group is wholly active or not.
-    const bool active = u < units;
-    const u32x4* src = x + static_cast<size_t>(t) * (hidden >> 3);
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (active) {
-      a = src[2 * u];
-      b = src[2 * u + 1];
+  const int wave = wave_index();
+  const int topk = fc.topk;
+  const int nitems = num_tokens * groups;
+  if constexpr (!kShared) {   // each wavefront ranks its token's slots itself
+    for (int item = blockIdx.x; item < nitems; item += work_blocks) {
+      const int t = item / groups;
+      const int slice = (item - t * groups) * kFixedWaves + wave;
+      if (slice >= slices) continue;
+      const WaveRows rows{fc, slice == 0};
+      payload_item<kDtype>(x, rows, out, scales, t, slice, hidden, topk);
     }
-    float f[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
-                   bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
-                   bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
-                   bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(f[i]));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));
-    m = fmaxf(m, __shfl_xor(m, 4, 64));
-    const float scale = m / 448.0f;
-    if (m > 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) f[i] = __builtin_amdgcn_fmed3f(f[i] / scale, -448.0f, 448.0f);
-    }
-    u32x4 q;
-    q.x = pack_e4m3(f[0], f[1], f[2], f[3]);
-    q.y = pack_e4m3(f[4], f[5], f[6], f[7]);
-    q.z = pack_e4m3(f[8], f[9], f[10], f[11]);
-    q.w = pack_e4m3(f[12], f[13], f[14], f[15]);
-    const bool scale_lane = active && (lane & 7) == 0;
-    for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
-      int p[kSlotBatch];
-      src_rows.rows_of(t, j0, slice == 0, p);
-#pragma unroll
-      for (int jj = 0; jj < kSlotBatch; ++jj) {
-        if (p[jj] < 0) continue;
-        if (active) store_row(&out[static_cast<size_t>(p[jj]) * units + u], q);
-        if (scale_lane) scales[static_cast<size_t>(p[jj]) * nscale + (u >> 3)] = scale;
-      }
-    }
+    return;
   }
-}
-
-// MXFP8 (OCP Microscaling v1.0, E4M3 elements): 32-channel blocks share an
-// E8M0 power-of-two scale. A lane holds 16 channels, so a block is a lane
-// pair; shared = floor(log2 amax) - 8 (8: exponent of E4M3's largest normal),
-// clamped to E8M0's [-127, 127], read off amax's fp32 bit fields. Elements are
-// x * 2^-shared (exact: a power of two, and every product that can round to a
-// nonzero code is a normal fp32), clamped to +-448 and converted by the
-// hardware fp32 -> fp8 instruction (round-to-nearest-even). An all-zero block
-// gets code 0 and signed-zero elements. Four E8M0 bytes go out per dword
-// store. The Hybrid-EP news item ("Efficiency Numbers") reports its Qwen3 run
-// in MXFP8.
-template <class Rows>
-__global__ __launch_bounds__(64 * kItemWaves) void dispatch_mxfp8_kernel(
-    const u32x4* __restrict__ x, Rows src_rows, u32x4* __restrict__ out,
-    uint32_t* __restrict__ scales, int num_tokens, int hidden, int slices, int payload_blocks) {
-  if constexpr (Rows::kCountsBlock) {
-    if (static_cast<int>(blockIdx.x) == payload_blocks) {
-      src_rows.counts_block(num_tokens);
-      return;
-    }
-  }
-  const int lane = threadIdx.x & 63;
-  const int units = hidden >> 4;           // 16 channels per lane
-  const int scale_words = hidden >> 7;     // 4 one-byte scales per dword, per row
-  const int nitems = num_tokens * slices;
-  const int topk = src_rows.topk;
-  for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
-       item += payload_blocks * kItemWaves) {
-    const int t = item / slices;
-    const int slice = item - t * slices;
-    const int u = slice * 64 + lane;
-    // units is a multiple of 8, so each 8-lane group is wholly active or not.
-    const bool active = u < units;
-    const u32x4* src = x + static_cast<size_t>(t) * (hidden >> 3);
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (active) {
-      a = src[2 * u];
-      b = src[2 * u + 1];
-    }
-    float f[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
-                   bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
-                   bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
-                   bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
-    float m = 0.0f;
+  const SharedRows rows{s_pos, topk};
+  for (int item = blockIdx.x; item < nitems; item += work_blocks) {
+    const int t = item / groups;
+    const int g = item - t * groups;
+    const int own = fc.rank_share(t, wave, kFixedWaves, s_part[wave]);
+    __syncthreads();
+    const int j = threadIdx.x;   // lanes 0 .. topk-1 of wavefront 0, which hold the ids
+    if (j < topk) {
+      int rank = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(f[i]));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    const uint32_t mb = __float_as_uint(m);
-    int shared = -127;
-    if (mb != 0u) {
-      const int fl = mb >= 0x00800000u ? static_cast<int>(mb >> 23) - 127   // normal
-                                       : 31 - __clz(mb) - 149;                // subnormal
-      shared = fl - 8 < -127 ? -127 : (fl - 8 > 127 ? 127 : fl - 8);
+      for (int w = 0; w < kFixedWaves; ++w) rank += s_part[w][j];
+      const int p = fc.row_of(own, rank);
+      s_pos[j] = p;
+      if (g == 0) fc.pos[t * topk + j] = p;
     }
-    const float inv = __uint_as_float(static_cast<uint32_t>(127 - shared) << 23);   // 2^-shared
-#pragma unroll
-    for (int i = 0; i < 16; ++i) f[i] = __builtin_amdgcn_fmed3f(f[i] * inv, -448.0f, 448.0f);
-    u32x4 q;
-    q.x = pack_e4m3(f[0], f[1], f[2], f[3]);
-    q.y = pack_e4m3(f[4], f[5], f[6], f[7]);
-    q.z = pack_e4m3(f[8], f[9], f[10], f[11]);
-    q.w = pack_e4m3(f[12], f[13], f[14], f[15]);
-    // Lane 8i gathers the codes of blocks u/2 .. u/2+3 (lanes 8i, 8i+2, 8i+4, 8i+6).
-    const uint32_t code = static_cast<uint32_t>(shared + 127);
-    const uint32_t c1 = __shfl(code, lane + 2, 64);
-    const uint32_t c2 = __shfl(code, lane + 4, 64);
-    const uint32_t c3 = __shfl(code, lane + 6, 64);
-    const uint32_t word = code | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    const bool scale_lane = active && (lane & 7) == 0;
-    for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
-      int p[kSlotBatch];
-      src_rows.rows_of(t, j0, slice == 0, p);
-#pragma unroll
-      for (int jj = 0; jj < kSlotBatch; ++jj) {
-        if (p[jj] < 0) continue;
-        if (active) store_row(&out[static_cast<size_t>(p[jj]) * units + u], q);
-        if (scale_lane) scales[static_cast<size_t>(p[jj]) * scale_words + (u >> 3)] = word;
-      }
-    }
+    __syncthreads();
+    const int slice = g * kFixedWaves + wave;
+    if (slice < slices) payload_item<kDtype>(x, rows, out, scales, t, slice, hidden, topk);
+    __syncthreads();   // s_part and s_pos are rewritten for the next item
   }
 }
 
@@ -425,38 +634,26 @@ hipError_t launch_rank_meta(const int32_t* d_idx, const float* d_w, const int32_
   return hipGetLastError();
 }
 
-// Grid of a payload kernel: work-item workgroups (capped by max_blocks),
-// plus the counts workgroup for the fixed-capacity layout.
-template <class Rows>
-hipError_t launch_payload(int dtype, const void* d_x, const Rows& src_rows, void* d_out,
-                          void* d_scales, int num_tokens, int hidden, int max_blocks,
-                          hipStream_t stream) {
-  const int per_lane = dtype == MOE_DTYPE_BF16 ? 8 : 16;   // channels per lane
-  const int slices = (hidden / per_lane + 63) / 64;
-  const int payload = num_tokens == 0 ? 0
-                      : static_cast<int>(item_grid(int64_t(num_tokens) * slices, max_blocks).x);
-  const int blocks = payload + (Rows::kCountsBlock ? 1 : 0);
-  if (blocks == 0) return hipSuccess;
-  const dim3 grid(blocks), block(64 * kItemWaves);
-  const u32x4* x = static_cast<const u32x4*>(d_x);
-  u32x4* out = static_cast<u32x4*>(d_out);
-  if (dtype == MOE_DTYPE_BF16)
-    hipLaunchKernelGGL(dispatch_bf16_kernel<Rows>, grid, block, 0, stream, x, src_rows, out,
-                       num_tokens, hidden / 8, slices, payload);
-  else if (dtype == MOE_DTYPE_FP8_E4M3)
-    hipLaunchKernelGGL(dispatch_fp8_kernel<Rows>, grid, block, 0, stream, x, src_rows, out,
-                       static_cast<float*>(d_scales), num_tokens, hidden, slices, payload);
-  else
-    hipLaunchKernelGGL(dispatch_mxfp8_kernel<Rows>, grid, block, 0, stream, x, src_rows, out,
-                       static_cast<uint32_t*>(d_scales), num_tokens, hidden, slices, payload);
-  return hipGetLastError();
-}
-
 hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, void* d_out,
                            void* d_scales, int64_t rows, int num_tokens, int topk, int hidden,
                            int max_blocks, hipStream_t stream) {
-  return launch_payload(dtype, d_x, TableRows{d_pos, topk, rows}, d_out, d_scales, num_tokens,
-                        hidden, max_blocks, stream);
+  if (num_tokens == 0) return hipSuccess;
+  const int slices = (hidden / lane_channels(dtype) + 63) / 64;
+  const dim3 grid = item_grid(int64_t(num_tokens) * slices, max_blocks), block(64 * kItemWaves);
+  const int payload = static_cast<int>(grid.x);
+  const u32x4* x = static_cast<const u32x4*>(d_x);
+  u32x4* out = static_cast<u32x4*>(d_out);
+  const TableRows tr{d_pos, topk, rows};
+  if (dtype == MOE_DTYPE_BF16)
+    hipLaunchKernelGGL(dispatch_bf16_kernel<TableRows>, grid, block, 0, stream, x, tr, out,
+                       num_tokens, hidden / 8, slices, payload);
+  else if (dtype == MOE_DTYPE_FP8_E4M3)
+    hipLaunchKernelGGL(dispatch_fp8_kernel<TableRows>, grid, block, 0, stream, x, tr, out,
+                       static_cast<float*>(d_scales), num_tokens, hidden, slices, payload);
+  else
+    hipLaunchKernelGGL(dispatch_mxfp8_kernel<TableRows>, grid, block, 0, stream, x, tr, out,
+                       static_cast<uint32_t*>(d_scales), num_tokens, hidden, slices, payload);
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch_fixed(int dtype, const void* d_x, const int32_t* d_idx,
@@ -464,8 +661,33 @@ hipError_t launch_dispatch_fixed(int dtype, const void* d_x, const int32_t* d_id
                                  int32_t* d_pos, int32_t* d_counts, int32_t* d_status,
                                  void* d_out, void* d_scales, int hidden, int max_blocks,
                                  hipStream_t stream) {
-  const FixedCapacityRows src{d_idx, topk, num_experts, capacity, d_pos, d_counts, d_status};
-  return launch_payload(dtype, d_x, src, d_out, d_scales, num_tokens, hidden, max_blocks, stream);
+  const int slices = (hidden / lane_channels(dtype) + 63) / 64;
+  const int groups = (slices + kFixedWaves - 1) / kFixedWaves;
+  int work_blocks = num_tokens * groups;
+  if (max_blocks > 0 && work_blocks > max_blocks) work_blocks = max_blocks;
+  const dim3 grid(work_blocks + 1), block(64 * kFixedWaves);   // + the counts workgroup
+  const FixedCapacity fc{d_idx, topk, num_experts, capacity, d_pos, d_counts, d_status};
+  const u32x4* x = static_cast<const u32x4*>(d_x);
+  u32x4* out = static_cast<u32x4*>(d_out);
+  // Up to kFixedSharedFrom tokens each wavefront ranks its slots alone (no
+  // barrier); from there on a workgroup's wavefronts share the count.
+  const bool shared = num_tokens >= kFixedSharedFrom;
+#define MOE_FIXED_LAUNCH(DT, SHARED, SCALES)                                                   \
+  hipLaunchKernelGGL((dispatch_fixed_kernel<DT, SHARED>), grid, block, 0, stream, x, fc, out,     \
+                     static_cast<SCALES*>(d_scales), num_tokens, hidden, slices, groups,          \
+                     work_blocks)
+  if (dtype == MOE_DTYPE_BF16) {
+    if (shared) MOE_FIXED_LAUNCH(MOE_DTYPE_BF16, true, float);
+    else MOE_FIXED_LAUNCH(MOE_DTYPE_BF16, false, float);
+  } else if (dtype == MOE_DTYPE_FP8_E4M3) {
+    if (shared) MOE_FIXED_LAUNCH(MOE_DTYPE_FP8_E4M3, true, float);
+    else MOE_FIXED_LAUNCH(MOE_DTYPE_FP8_E4M3, false, float);
+  } else {
+    if (shared) MOE_FIXED_LAUNCH(MOE_DTYPE_MXFP8_E4M3, true, uint32_t);
+    else MOE_FIXED_LAUNCH(MOE_DTYPE_MXFP8_E4M3, false, uint32_t);
+  }
+#undef MOE_FIXED_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace moe
