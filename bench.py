@@ -421,8 +421,9 @@ def main():
         decode["step_graph_us"] = sustained_us(lambda i: graph.replay(), args.sustained_iters)
         del graph, dsets, hd
 
-        # Decode-time dispatch against layout + dispatch over batch sizes (bf16,
-        # capacity = T, so nothing is dropped).
+        # Decode-time dispatch (fixed capacity = T, nothing dropped) and the
+        # one-launch packed layout + dispatch against the two calls, over batch
+        # sizes (bf16).
         scaling = {}
         for Tn in (32, 128, 512, 1024):
             hn = Handle(Tn, H, k, E, R, device=dev)
@@ -437,6 +438,8 @@ def main():
             scaling[str(Tn)] = {
                 "ll_dispatch_bf16_us": sustained_us(lambda i: hn.ll_dispatch(ni, nx, Tn, out=n_ll),
                                                     args.sustained_iters),
+                "layout_dispatch_bf16_us": sustained_us(
+                    lambda i: hn.layout_dispatch(ni, nx, out=n_std), args.sustained_iters),
                 "layout_plus_dispatch_bf16_us": sustained_us(n_standard, args.sustained_iters)}
             del hn, n_ll, n_std
         decode["by_tokens"] = scaling

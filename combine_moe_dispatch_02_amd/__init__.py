@@ -23,7 +23,8 @@ from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP8_E4M3, MOE
 __all__ = ["Handle", "MoeError", "MoeConfig", "moe_workspace_bytes", "moe_handle_create",
            "moe_handle_destroy", "moe_dispatch_layout", "moe_layout_view", "moe_dispatch",
            "moe_combine", "moe_rank_layout", "moe_rank_layout_view", "moe_dispatch_ranks",
-           "moe_combine_ranks", "moe_set_max_workgroups", "moe_route", "moe_ll_dispatch",
+           "moe_combine_ranks", "moe_set_max_workgroups", "moe_route", "moe_layout_dispatch",
+           "moe_ll_dispatch",
            "moe_ll_view", "moe_ll_combine", "moe_status_string", "moe_last_error",
            "MOE_DTYPE_BF16", "MOE_DTYPE_MXFP8_E4M3", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
            "MOE_EP_LL_MAX_TOKENS",
@@ -166,6 +167,16 @@ def moe_route(h: int, logits: torch.Tensor, score: int, topk_idx: torch.Tensor,
                                      _stream(stream, logits.device)))
 
 
+def moe_layout_dispatch(h: int, topk_idx: torch.Tensor, x: torch.Tensor, dtype: int,
+                        out: torch.Tensor, scales: torch.Tensor | None, stream=None) -> None:
+    pi = _ptr(topk_idx, torch.int32, "topk_idx")
+    px, po, ps = _payload_ptrs(x, dtype, out, scales)
+    _lib.check(_lib.load().moe_layout_dispatch(
+        ctypes.c_void_p(h), ctypes.c_void_p(pi), int(topk_idx.shape[0]), ctypes.c_void_p(px),
+        int(dtype), ctypes.c_void_p(po), ctypes.c_void_p(ps), out.shape[0],
+        _stream(stream, x.device)))
+
+
 def moe_ll_dispatch(h: int, topk_idx: torch.Tensor, capacity: int, x: torch.Tensor, dtype: int,
                     out: torch.Tensor, scales: torch.Tensor | None, stream=None) -> None:
     pi = _ptr(topk_idx, torch.int32, "topk_idx")
@@ -287,6 +298,29 @@ class Handle:
             topk_w = torch.empty((T, self.topk), dtype=torch.float32, device=self.device)
         moe_route(self.h, logits, code, topk_idx, topk_w, stream)
         return topk_idx, topk_w
+
+    # ---- layout and dispatch in one launch (small batches)
+    def layout_dispatch(self, topk_idx: torch.Tensor, x: torch.Tensor, dtype: str = "bf16",
+                        out=None, scales=None, stream=None):
+        """layout() + dispatch() in one launch: rows [T*k, H] bf16, or (codes, scales)."""
+        _ptr(topk_idx, torch.int32, "topk_idx", self.device)
+        _ptr(x, torch.bfloat16, "x", self.device)
+        code = {"bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_E4M3,
+                "mxfp8": MOE_DTYPE_MXFP8_E4M3}[dtype]
+        rows = int(topk_idx.shape[0]) * self.topk
+        if out is None:
+            out = torch.empty((rows, self.hidden),
+                              dtype=torch.bfloat16 if code == MOE_DTYPE_BF16 else torch.uint8,
+                              device=self.device)
+        if scales is None and code == MOE_DTYPE_FP8_E4M3:
+            scales = torch.empty((rows, self.hidden // MOE_EP_FP8_BLOCK), dtype=torch.float32,
+                                 device=self.device)
+        if scales is None and code == MOE_DTYPE_MXFP8_E4M3:
+            scales = torch.empty((rows, self.hidden // MOE_MX_BLOCK), dtype=torch.uint8,
+                                 device=self.device)
+        moe_layout_dispatch(self.h, topk_idx, x, code, out, scales, stream)
+        self.num_tokens = int(topk_idx.shape[0])
+        return out if code == MOE_DTYPE_BF16 else (out, scales)
 
     # ---- decode-time (fixed-capacity) dispatch and combine
     def ll_dispatch(self, topk_idx: torch.Tensor, x: torch.Tensor, capacity: int,

@@ -27,7 +27,8 @@ MOE_SCORE_SIGMOID = 1
 EXPORTS = ("moe_workspace_bytes", "moe_handle_create", "moe_handle_destroy",
            "moe_dispatch_layout", "moe_layout_view", "moe_dispatch", "moe_combine",
            "moe_rank_layout", "moe_rank_layout_view", "moe_dispatch_ranks", "moe_combine_ranks",
-           "moe_set_max_workgroups", "moe_route", "moe_ll_dispatch", "moe_ll_view",
+           "moe_set_max_workgroups", "moe_route", "moe_layout_dispatch", "moe_ll_dispatch",
+           "moe_ll_view",
            "moe_ll_combine", "moe_status_string", "moe_last_error")
 
 
@@ -98,6 +99,7 @@ def load() -> ctypes.CDLL:
         "moe_combine_ranks": (ctypes.c_int, [vp, vp, i64, vp, vp]),
         "moe_set_max_workgroups": (ctypes.c_int, [vp, i32]),
         "moe_route": (ctypes.c_int, [vp, vp, i32, ctypes.c_int, vp, vp, vp]),
+        "moe_layout_dispatch": (ctypes.c_int, [vp, vp, i32, vp, ctypes.c_int, vp, vp, i64, vp]),
         "moe_ll_dispatch": (ctypes.c_int, [vp, vp, i32, i32, vp, ctypes.c_int, vp, vp, i64, vp]),
         "moe_ll_view": (ctypes.c_int, [vp, ctypes.POINTER(MoeLlView)]),
         "moe_ll_combine": (ctypes.c_int, [vp, vp, i64, vp, vp, vp]),

@@ -398,38 +398,65 @@ constexpr int kCountLoads = 8;
 constexpr int kFixedWaves = 4;   // wavefronts (column slices) per decode-time workgroup
 constexpr int kFixedSharedFrom = 256;   // tokens from which a workgroup shares the rank count
 
-struct FixedCapacity {
+// Layout computed inside the dispatch kernel, in one of two forms:
+//   fixed capacity (kPacked = false): expert e owns rows [e*C, (e+1)*C); a
+//     slot's row is e*C + r, r = earlier slots with its id, dropped from C on;
+//   packed (kPacked = true): the standard layout -- a slot's row is the number
+//     of valid slots with a smaller id plus r, so expert e's rows start at
+//     offsets_e[e] -- exactly what the two layout kernels produce.
+template <bool kPacked>
+struct FusedLayout {
   const int32_t* idx;   // [T, k] expert ids
-  int topk, num_experts, capacity;
+  int topk, num_experts, capacity;   // capacity: fixed form only
   int32_t* pos;         // [T, k] rows, recorded for combine
-  int32_t* counts;      // [E] rows received per expert
-  int32_t* status;      // [4] invalid, placed, T, dropped
+  int32_t* counts;      // [E] rows per expert (at most C in the fixed form)
+  int32_t* status;      // fixed: invalid, placed, T, dropped; packed: invalid, rows, T, 0
+  // packed form only
+  int32_t* offsets;        // [E + 1]
+  int32_t* group_counts;   // [R]
+  int32_t* group_offsets;  // [R + 1]
+  int32_t* src;            // [T * k] token of each row, -1 past the valid total
+  int num_groups;          // R
+  int per_group;           // E / R
 
-  // Per-lane match counts for slots j0 .. j0+kSlotBatch-1 of token t (ids e[]):
-  // matches among the earlier tokens' slots [0, t*k) in chunks of 64 ids
-  // strided by `waves` wavefronts starting at chunk `wave` (kRankLoads chunks
-  // in flight), plus, for wavefront 0, the token's own earlier slots (`own`:
-  // this token's id of slot `lane`). One compare and one add per id and slot.
+  // Per-lane counts for slots j0 .. j0+kSlotBatch-1 of token t (ids e[]),
+  // one packed counter per slot: low 16 bits = earlier slots with the same
+  // id, high 16 bits (packed form) = valid slots with a smaller id (both below
+  // 2^15 since T*k <= MOE_EP_LL_MAX_TOKENS * MOE_EP_MAX_TOPK). The ids are
+  // read in chunks of 64, strided by `waves` wavefronts starting at chunk
+  // `wave` (kRankLoads chunks in flight), over the earlier tokens' slots
+  // [0, t*k) -- or all slots for the packed form; wavefront 0 adds the
+  // token's own earlier slots (`own`: this token's id of slot `lane`).
   __device__ __forceinline__ void count_batch(int t, int j0, int wave, int waves, int own,
-                                              const int (&e)[kSlotBatch],
+                                              int slots, const int (&e)[kSlotBatch],
                                               uint32_t (&cnt)[kSlotBatch]) const {
     const int base = t * topk;
     const int lane = threadIdx.x & 63;
+    const int end = kPacked ? slots : base;
 #pragma unroll
     for (int jj = 0; jj < kSlotBatch; ++jj) cnt[jj] = 0u;
     const int stride = waves * 64;
-    for (int c = wave * 64; c < base; c += stride * kRankLoads) {
+    for (int c = wave * 64; c < end; c += stride * kRankLoads) {
       int id[kRankLoads];
 #pragma unroll
       for (int q = 0; q < kRankLoads; ++q) {
         const int s = c + q * stride + lane;
-        id[q] = idx[s < base ? s : 0];
-        if (s >= base) id[q] = -1;
+        id[q] = idx[s < end ? s : 0];
+        if (s >= end) id[q] = -1;
       }
 #pragma unroll
-      for (int q = 0; q < kRankLoads; ++q)
+      for (int q = 0; q < kRankLoads; ++q) {
+        const bool earlier = c + q * stride + lane < base;
 #pragma unroll
-        for (int jj = 0; jj < kSlotBatch; ++jj) cnt[jj] += id[q] == e[jj] ? 1u : 0u;
+        for (int jj = 0; jj < kSlotBatch; ++jj) {
+          if (kPacked) {
+            cnt[jj] += (earlier && id[q] == e[jj]) ? 1u : 0u;
+            cnt[jj] += static_cast<unsigned>(id[q]) < static_cast<unsigned>(e[jj]) ? 0x10000u : 0u;
+          } else {
+            cnt[jj] += id[q] == e[jj] ? 1u : 0u;
+          }
+        }
+      }
     }
     if (wave == 0) {
 #pragma unroll
@@ -445,23 +472,32 @@ struct FixedCapacity {
       e[jj] = idx[base + (j0 + jj < topk ? j0 + jj : topk - 1)];
   }
 
-  __device__ __forceinline__ int row_of(int e, int rank) const {
-    return static_cast<unsigned>(e) < static_cast<unsigned>(num_experts) && rank < capacity
-               ? e * capacity + rank
-               : -1;
+  // Row of a slot with id e from its summed counter, or -1.
+  __device__ __forceinline__ int row_of(int e, uint32_t sum) const {
+    if (static_cast<unsigned>(e) >= static_cast<unsigned>(num_experts)) return -1;
+    const int same = static_cast<int>(sum & 0xFFFFu);
+    if (kPacked) return static_cast<int>(sum >> 16) + same;
+    return same < capacity ? e * capacity + same : -1;
   }
 
-  // This wavefront's share of the ranks of token t's slots (one of `waves`),
-  // summed over its lanes into part[slot]. Returns this token's id of slot
-  // `lane` (lanes < topk).
-  __device__ __forceinline__ int rank_share(int t, int wave, int waves, int32_t* part) const {
+  // Record slot j of token t at row p (the one wavefront or thread that owns it).
+  __device__ __forceinline__ void record(int t, int j, int p) const {
+    pos[t * topk + j] = p;
+    if (kPacked && p >= 0) src[p] = t;
+  }
+
+  // This wavefront's share of the counters of token t's slots (one of
+  // `waves`), summed over its lanes into part[slot]. Returns this token's id
+  // of slot `lane` (lanes < topk).
+  __device__ __forceinline__ int rank_share(int t, int wave, int waves, int slots,
+                                            int32_t* part) const {
     const int lane = threadIdx.x & 63;
     const int own = idx[t * topk + (lane < topk ? lane : 0)];
     for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
       int e[kSlotBatch];
       uint32_t cnt[kSlotBatch];
       batch_ids(t, j0, e);
-      count_batch(t, j0, wave, waves, own, e, cnt);
+      count_batch(t, j0, wave, waves, own, slots, e, cnt);
 #pragma unroll
       for (int jj = 0; jj < kSlotBatch; ++jj) {
         const uint32_t sum = wave_sum_u32(cnt[jj]);
@@ -471,11 +507,14 @@ struct FixedCapacity {
     return own;
   }
 
-  // Run by the grid's last workgroup: histogram of all slots in LDS, then
-  // per-expert counts (clamped to the capacity) and the status words.
+  // Run by the grid's last workgroup: histogram of all slots in LDS, then the
+  // per-expert counts and the status words; in the packed form also the
+  // exclusive scan over experts, the per-rank counts and offsets, and -1 for
+  // the row sources past the valid total.
   __device__ void counts_block(int num_tokens) const {
     __shared__ int hist[MOE_EP_MAX_EXPERTS];
     __shared__ int tally[2];   // invalid slots, dropped slots
+    __shared__ int s_wsum[kFixedWaves];
     const int tid = threadIdx.x, nthreads = blockDim.x;
     for (int e = tid; e < num_experts; e += nthreads) hist[e] = 0;
     if (tid < 2) tally[tid] = 0;
@@ -502,74 +541,124 @@ struct FixedCapacity {
     }
     if (bad) atomicAdd(&tally[0], bad);
     __syncthreads();
-    int drop = 0;
-    for (int e = tid; e < num_experts; e += nthreads) {
-      const int c = hist[e];
-      counts[e] = c < capacity ? c : capacity;
-      drop += c > capacity ? c - capacity : 0;
+    if (!kPacked) {
+      int drop = 0;
+      for (int e = tid; e < num_experts; e += nthreads) {
+        const int c = hist[e];
+        counts[e] = c < capacity ? c : capacity;
+        drop += c > capacity ? c - capacity : 0;
+      }
+      if (drop) atomicAdd(&tally[1], drop);
+      __syncthreads();
+      if (tid == 0) {
+        status[0] = tally[0];
+        status[1] = slots - tally[0] - tally[1];
+        status[2] = num_tokens;
+        status[3] = tally[1];
+      }
+      return;
     }
-    if (drop) atomicAdd(&tally[1], drop);
+    // Exclusive scan over experts: thread tid sums experts [tid*c, tid*c + c),
+    // c = ceil(E / nthreads) <= 4; a wavefront scan and the wavefront totals
+    // give each thread its start.
+    const int lane = tid & 63, wave = tid >> 6;
+    const int c = (num_experts + nthreads - 1) / nthreads;
+    const int e0 = tid * c;
+    int local = 0;
+    for (int e = e0; e < e0 + c && e < num_experts; ++e) local += hist[e];
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += up;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wave; ++w) run += s_wsum[w];
+    int total = 0;
+    for (int w = 0; w < nthreads / 64; ++w) total += s_wsum[w];
+    __syncthreads();   // everyone has read s_wsum and hist[e0 .. e0+c)
+    for (int e = e0; e < e0 + c && e < num_experts; ++e) {
+      const int n = hist[e];
+      counts[e] = n;
+      offsets[e] = run;
+      hist[e] = run;   // keep the offsets for the per-rank figures
+      run += n;
+    }
+    __syncthreads();
+    for (int r = tid; r < num_groups; r += nthreads) {
+      const int a = hist[r * per_group];
+      const int b = r + 1 < num_groups ? hist[(r + 1) * per_group] : total;
+      group_counts[r] = b - a;
+      group_offsets[r] = a;
+    }
+    for (int p = total + tid; p < slots; p += nthreads) src[p] = -1;
     if (tid == 0) {
+      offsets[num_experts] = total;
+      group_offsets[num_groups] = total;
       status[0] = tally[0];
-      status[1] = slots - tally[0] - tally[1];
+      status[1] = total;
       status[2] = num_tokens;
-      status[3] = tally[1];
+      status[3] = 0;
     }
   }
 };
-
-// Decode-time rows computed by one wavefront alone (small batches): the whole
-// count of earlier matching ids, no LDS and no barrier. `record` makes it
-// store the token's rows for combine (one wavefront per token does).
+// Fused-layout rows computed by one wavefront alone (small batches): the whole
+// count, no LDS and no barrier. `record` makes it store the token's rows
+// (one wavefront per token does).
+template <bool kPacked>
 struct WaveRows {
-  FixedCapacity fc;
+  FusedLayout<kPacked> fl;
+  int slots;
   bool record;
   __device__ __forceinline__ void rows_of(int t, int j0, int (&p)[kSlotBatch]) const {
     const int lane = threadIdx.x & 63;
-    const int topk = fc.topk;
-    const int own = fc.idx[t * topk + (lane < topk ? lane : 0)];
+    const int topk = fl.topk;
+    const int own = fl.idx[t * topk + (lane < topk ? lane : 0)];
     int e[kSlotBatch];
     uint32_t cnt[kSlotBatch];
-    fc.batch_ids(t, j0, e);
-    fc.count_batch(t, j0, 0, 1, own, e, cnt);
+    fl.batch_ids(t, j0, e);
+    fl.count_batch(t, j0, 0, 1, own, slots, e, cnt);
     int mine = -1;
 #pragma unroll
     for (int jj = 0; jj < kSlotBatch; ++jj) {
-      const int rank = static_cast<int>(wave_sum_u32(cnt[jj]));
-      p[jj] = j0 + jj < topk ? fc.row_of(e[jj], rank) : -1;
+      const uint32_t sum = wave_sum_u32(cnt[jj]);
+      p[jj] = j0 + jj < topk ? fl.row_of(e[jj], sum) : -1;
       if (lane == jj) mine = p[jj];
     }
-    if (record && lane < kSlotBatch && j0 + lane < topk) fc.pos[t * topk + j0 + lane] = mine;
+    if (record && lane < kSlotBatch && j0 + lane < topk) fl.record(t, j0 + lane, mine);
   }
 };
 
-// Decode-time dispatch: a workgroup of kFixedWaves wavefronts takes one
-// (token, group of kFixedWaves column slices) item, looping over items when
-// the grid is capped. Its wavefronts split the token's rank count, add their
-// shares through LDS, and then each moves one slice; the group holding slice
-// 0 records the token's rows. The grid's last workgroup publishes the counts.
-// No workgroup waits for another.
-template <int kDtype, bool kShared>
-__global__ __launch_bounds__(64 * kFixedWaves) void dispatch_fixed_kernel(
-    const u32x4* __restrict__ x, FixedCapacity fc, u32x4* __restrict__ out,
+// Dispatch with the layout computed in the same launch: a workgroup of
+// kFixedWaves wavefronts takes one (token, group of kFixedWaves column
+// slices) item, looping over items when the grid is capped; each wavefront
+// moves one slice, and the group holding slice 0 records the token's rows.
+// kShared: the wavefronts split the count and add their shares through LDS
+// (larger batches); otherwise each counts alone (no barrier). The grid's last
+// workgroup publishes the counts. No workgroup waits for another.
+template <int kDtype, bool kPacked, bool kShared>
+__global__ __launch_bounds__(64 * kFixedWaves) void dispatch_fused_kernel(
+    const u32x4* __restrict__ x, FusedLayout<kPacked> fl, u32x4* __restrict__ out,
     ScalePtr<kDtype> __restrict__ scales, int num_tokens, int hidden, int slices, int groups,
     int work_blocks) {
   __shared__ int32_t s_part[kFixedWaves][MOE_EP_MAX_TOPK];
   __shared__ int32_t s_pos[MOE_EP_MAX_TOPK];
   if (static_cast<int>(blockIdx.x) == work_blocks) {
-    fc.counts_block(num_tokens);
+    fl.counts_block(num_tokens);
     return;
   }
   const int wave = wave_index();
-  const int topk = fc.topk;
+  const int topk = fl.topk;
   const int nitems = num_tokens * groups;
+  const int slots = num_tokens * topk;
   if constexpr (!kShared) {   // each wavefront ranks its token's slots itself
     for (int item = blockIdx.x; item < nitems; item += work_blocks) {
       const int t = item / groups;
       const int slice = (item - t * groups) * kFixedWaves + wave;
       if (slice >= slices) continue;
-      const WaveRows rows{fc, slice == 0};
+      const WaveRows<kPacked> rows{fl, slots, slice == 0};
       payload_item<kDtype>(x, rows, out, scales, t, slice, hidden, topk);
     }
     return;
@@ -578,16 +667,16 @@ __global__ __launch_bounds__(64 * kFixedWaves) void dispatch_fixed_kernel(
   for (int item = blockIdx.x; item < nitems; item += work_blocks) {
     const int t = item / groups;
     const int g = item - t * groups;
-    const int own = fc.rank_share(t, wave, kFixedWaves, s_part[wave]);
+    const int own = fl.rank_share(t, wave, kFixedWaves, slots, s_part[wave]);
     __syncthreads();
     const int j = threadIdx.x;   // lanes 0 .. topk-1 of wavefront 0, which hold the ids
     if (j < topk) {
-      int rank = 0;
+      uint32_t sum = 0u;
 #pragma unroll
-      for (int w = 0; w < kFixedWaves; ++w) rank += s_part[w][j];
-      const int p = fc.row_of(own, rank);
+      for (int w = 0; w < kFixedWaves; ++w) sum += static_cast<uint32_t>(s_part[w][j]);
+      const int p = fl.row_of(own, sum);
       s_pos[j] = p;
-      if (g == 0) fc.pos[t * topk + j] = p;
+      if (g == 0) fl.record(t, j, p);
     }
     __syncthreads();
     const int slice = g * kFixedWaves + wave;
@@ -656,38 +745,60 @@ hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, voi
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_fixed(int dtype, const void* d_x, const int32_t* d_idx,
-                                 int num_tokens, int topk, int num_experts, int capacity,
-                                 int32_t* d_pos, int32_t* d_counts, int32_t* d_status,
-                                 void* d_out, void* d_scales, int hidden, int max_blocks,
-                                 hipStream_t stream) {
+namespace {
+
+template <bool kPacked>
+hipError_t launch_fused(int dtype, const void* d_x, const FusedLayout<kPacked>& fl,
+                        int num_tokens, void* d_out, void* d_scales, int hidden, int max_blocks,
+                        hipStream_t stream) {
   const int slices = (hidden / lane_channels(dtype) + 63) / 64;
   const int groups = (slices + kFixedWaves - 1) / kFixedWaves;
   int work_blocks = num_tokens * groups;
   if (max_blocks > 0 && work_blocks > max_blocks) work_blocks = max_blocks;
   const dim3 grid(work_blocks + 1), block(64 * kFixedWaves);   // + the counts workgroup
-  const FixedCapacity fc{d_idx, topk, num_experts, capacity, d_pos, d_counts, d_status};
   const u32x4* x = static_cast<const u32x4*>(d_x);
   u32x4* out = static_cast<u32x4*>(d_out);
-  // Up to kFixedSharedFrom tokens each wavefront ranks its slots alone (no
+  // Below kFixedSharedFrom tokens each wavefront ranks its slots alone (no
   // barrier); from there on a workgroup's wavefronts share the count.
   const bool shared = num_tokens >= kFixedSharedFrom;
-#define MOE_FIXED_LAUNCH(DT, SHARED, SCALES)                                                   \
-  hipLaunchKernelGGL((dispatch_fixed_kernel<DT, SHARED>), grid, block, 0, stream, x, fc, out,     \
-                     static_cast<SCALES*>(d_scales), num_tokens, hidden, slices, groups,          \
+#define MOE_FUSED_LAUNCH(DT, SHARED, SCALES)                                                     \
+  hipLaunchKernelGGL((dispatch_fused_kernel<DT, kPacked, SHARED>), grid, block, 0, stream, x, fl, \
+                     out, static_cast<SCALES*>(d_scales), num_tokens, hidden, slices, groups,     \
                      work_blocks)
   if (dtype == MOE_DTYPE_BF16) {
-    if (shared) MOE_FIXED_LAUNCH(MOE_DTYPE_BF16, true, float);
-    else MOE_FIXED_LAUNCH(MOE_DTYPE_BF16, false, float);
+    if (shared) MOE_FUSED_LAUNCH(MOE_DTYPE_BF16, true, float);
+    else MOE_FUSED_LAUNCH(MOE_DTYPE_BF16, false, float);
   } else if (dtype == MOE_DTYPE_FP8_E4M3) {
-    if (shared) MOE_FIXED_LAUNCH(MOE_DTYPE_FP8_E4M3, true, float);
-    else MOE_FIXED_LAUNCH(MOE_DTYPE_FP8_E4M3, false, float);
+    if (shared) MOE_FUSED_LAUNCH(MOE_DTYPE_FP8_E4M3, true, float);
+    else MOE_FUSED_LAUNCH(MOE_DTYPE_FP8_E4M3, false, float);
   } else {
-    if (shared) MOE_FIXED_LAUNCH(MOE_DTYPE_MXFP8_E4M3, true, uint32_t);
-    else MOE_FIXED_LAUNCH(MOE_DTYPE_MXFP8_E4M3, false, uint32_t);
+    if (shared) MOE_FUSED_LAUNCH(MOE_DTYPE_MXFP8_E4M3, true, uint32_t);
+    else MOE_FUSED_LAUNCH(MOE_DTYPE_MXFP8_E4M3, false, uint32_t);
   }
-#undef MOE_FIXED_LAUNCH
+#undef MOE_FUSED_LAUNCH
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_fixed(int dtype, const void* d_x, const int32_t* d_idx,
+                                 int num_tokens, int topk, int num_experts, int capacity,
+                                 int32_t* d_pos, int32_t* d_counts, int32_t* d_status,
+                                 void* d_out, void* d_scales, int hidden, int max_blocks,
+                                 hipStream_t stream) {
+  const FusedLayout<false> fl{d_idx, topk, num_experts, capacity, d_pos, d_counts, d_status,
+                              nullptr, nullptr, nullptr, nullptr, 0, 1};
+  return launch_fused(dtype, d_x, fl, num_tokens, d_out, d_scales, hidden, max_blocks, stream);
+}
+
+hipError_t launch_layout_dispatch(int dtype, const void* d_x, const int32_t* d_idx,
+                                  int num_tokens, int topk, int num_experts, int num_ranks,
+                                  const LayoutArrays& a, void* d_out, void* d_scales, int hidden,
+                                  int max_blocks, hipStream_t stream) {
+  const FusedLayout<true> fl{d_idx, topk, num_experts, 0, a.pos, a.counts_e, a.status,
+                             a.offsets_e, a.counts_r, a.offsets_r, a.src_idx, num_ranks,
+                             num_experts / num_ranks};
+  return launch_fused(dtype, d_x, fl, num_tokens, d_out, d_scales, hidden, max_blocks, stream);
 }
 
 }  // namespace moe

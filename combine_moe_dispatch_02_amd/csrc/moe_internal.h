@@ -72,6 +72,14 @@ hipError_t launch_dispatch_fixed(int dtype, const void* d_x, const int32_t* d_id
                                  void* d_out, void* d_scales, int hidden, int max_blocks,
                                  hipStream_t stream);
 
+// Standard (packed) layout and dispatch in one launch, for small batches: the
+// same pos, src_idx, counts, offsets and status as launch_layout, and the
+// same rows as launch_dispatch.
+hipError_t launch_layout_dispatch(int dtype, const void* d_x, const int32_t* d_idx,
+                                  int num_tokens, int topk, int num_experts, int num_ranks,
+                                  const LayoutArrays& a, void* d_out, void* d_scales, int hidden,
+                                  int max_blocks, hipStream_t stream);
+
 // Router: top-k of each token's logits and the weights (score: moe_score_t).
 hipError_t launch_route(const float* d_logits, int num_tokens, int num_experts, int topk,
                         int score, int32_t* d_idx, float* d_w, hipStream_t stream);

@@ -237,6 +237,22 @@ int moe_set_max_workgroups(moe_handle_t h, int32_t max_workgroups);
 int moe_route(moe_handle_t h, const float* d_logits, int32_t num_tokens, int score,
               int32_t* d_topk_idx, float* d_topk_w, hipStream_t stream);
 
+/* Layout and dispatch in one launch, for small batches: exactly the results
+ * of moe_dispatch_layout followed by moe_dispatch (the standard packed
+ * layout: pos, src_idx, counts, offsets and status in the handle, the rows
+ * in d_out), computed by one kernel in which every workgroup derives its
+ * token's rows from the ids themselves -- a row is the number of valid slots
+ * with a smaller expert id plus the number of earlier slots with the same id.
+ * That count grows with num_tokens^2: from 640 tokens on the call enqueues
+ * the two layout kernels and the dispatch instead (same results, faster
+ * there), and num_tokens must lie in [0, min(max_tokens,
+ * MOE_EP_LL_MAX_TOKENS)]. dtype, d_out, d_scales and out_rows as in
+ * moe_dispatch. Leaves the handle's layout ready, as moe_dispatch_layout does:
+ * moe_layout_view, moe_dispatch and moe_combine follow as usual. */
+int moe_layout_dispatch(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_tokens,
+                        const void* d_x, int dtype, void* d_out, void* d_scales,
+                        int64_t out_rows, hipStream_t stream);
+
 /* Decode-time dispatch: layout and payload in one launch, into a buffer whose
  * shape does not depend on the routing -- the regime of DeepEP's low-latency
  * kernel family ("Inside the Nebius + PyTorch DeepSeek V3 recipe", section

@@ -198,6 +198,26 @@ def test_decode_time_calls_arguments(lib):
     lib.moe_handle_destroy(h)
 
 
+def test_layout_dispatch_arguments(lib):
+    h = make_handle(lib, cfg(T=2000, H=256, k=2, E=8, R=2))
+    fake = ctypes.c_void_p(1 << 24)
+    assert lib.moe_layout_dispatch(h, fake, 1025, fake, 0, fake, None, 1 << 20, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    assert "MOE_EP_LL_MAX_TOKENS" in lib.moe_last_error().decode()
+    assert lib.moe_layout_dispatch(h, fake, 16, fake, 0, fake, None, 31, None) == \
+        _lib.MOE_ERR_INVALID_ARG                                   # 16 tokens * top-2 rows needed
+    assert "out_rows" in lib.moe_last_error().decode()
+    assert lib.moe_layout_dispatch(h, fake, 16, fake, 5, fake, None, 32, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_layout_dispatch(h, fake, 16, fake, 1, fake, None, 32, None) == \
+        _lib.MOE_ERR_INVALID_ARG                                   # FP8 without scales
+    assert lib.moe_layout_dispatch(None, fake, 16, fake, 0, fake, None, 32, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    # a refused call leaves no layout behind
+    assert lib.moe_combine(h, fake, 1 << 10, fake, fake, None) == _lib.MOE_ERR_STATE
+    lib.moe_handle_destroy(h)
+
+
 def test_max_workgroups_arguments(lib):
     h = make_handle(lib)
     assert lib.moe_set_max_workgroups(h, 0) == _lib.MOE_OK

@@ -84,8 +84,13 @@ def test_random_config(seed):
     got_r = host_bits(h.combine_ranks(dev_bf16(part)))
     want_r, mag_r = oracle.combine_ranks(part, rl["rank_pos"], return_magnitude=True)
     assert_combine_close(got_r, want_r, mag_r, R)
-    # decode-time path (token limit 1024)
+    # layout and dispatch in one launch, and the decode-time path (token limit 1024)
     if T <= 1024:
+        h2 = Handle(T, H, k, E, R)
+        fused = h2.layout_dispatch(dev_i32(idx), dx)
+        v2 = {key: t.cpu().numpy().astype(np.int64) for key, t in h2.view().items()}
+        assert_layout_equal(v2, ref, T, k)
+        assert np.array_equal(host_bits(fused)[:n], oracle.dispatch_bf16(x, ref["pos"])[:n])
         out = h.ll_dispatch(dev_i32(idx), dx, C)
         v = h.ll_view()
         fc = oracle.layout_fixed_capacity(idx, E, C)
