@@ -19,6 +19,8 @@
 //      (all workgroups for the expert totals, earlier ones for its own base),
 //      scans the totals over experts, then walks its chunk again in slot order
 //      and assigns rows. Workgroup 0 also publishes counts and offsets.
+// When all slots fit one chunk (2048, e.g. 256 tokens at top-8) the place
+// kernel alone does both: its own per-wavefront counts are the totals.
 //
 // Inside a wavefront, lanes that hold the same expert id find each other with
 // ceil(log2 E) ballots (one per id bit); the lowest lane of each group does
@@ -152,7 +154,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(Buckets b, 
   for (int e = tid; e < b.nbuckets; e += kLayoutThreads) out[e] = s_hist[e];
 }
 
-template <bool kRanks>
+// kSingle: one workgroup holds every slot; no histogram kernel ran before it.
+template <bool kRanks, bool kSingle>
 __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b, LayoutOut o) {
   // s_cur[w * E + e]: wavefront w's running row cursor for bucket e.
   __shared__ int32_t s_cur[kLayoutWaves * MOE_EP_MAX_EXPERTS];
@@ -165,6 +168,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
   const int nblocks = gridDim.x;
 
   for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) s_cur[i] = 0;
+  if (kRanks && kSingle) {   // every (token, rank) starts as "not routed there"
+    const int cells = (b.slots / b.topk) * o.num_groups;
+    for (int i = tid; i < cells; i += kLayoutThreads) o.rank_pos[i] = -1;
+  }
 
   // This wavefront's slot ids, loaded first so that their latency overlaps
   // the histogram reads below.
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
 
   // Column sums of the per-workgroup histograms: the bucket totals, and the
   // part that earlier workgroups (earlier slots) contribute.
-  for (int e = tid; e < E; e += kLayoutThreads) {
+  for (int e = tid; e < E && !kSingle; e += kLayoutThreads) {
     int tot = 0, pre = 0;
 #pragma unroll 16
     for (int g = 0; g < nblocks; ++g) {
@@ -198,6 +205,18 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
     // Group leaders hold distinct ids within a step and the row belongs to
     // this wavefront alone, so a plain read-modify-write is race free.
     if (valid && lanes_below(peers[s]) == 0) my_cur[e] += __popcll(peers[s]);
+  }
+
+  if (kSingle) {   // the totals are the sums of the wavefronts' counts
+    __syncthreads();
+    for (int e = tid; e < E; e += kLayoutThreads) {
+      int tot = 0;
+#pragma unroll
+      for (int w = 0; w < kLayoutWaves; ++w) tot += s_cur[w * E + e];
+      s_off[e] = tot;
+      s_pre[e] = 0;
+    }
+    __syncthreads();
   }
 
   // Exclusive scan of the totals over buckets (two entries per thread, <= 1024).
@@ -307,12 +326,17 @@ int bits_for(int n) {
 template <bool kRanks>
 hipError_t launch_pass(const Buckets& b, const LayoutOut& o, hipStream_t stream) {
   const int nblocks = layout_blocks(b.slots);
+  if (nblocks == 1) {
+    hipLaunchKernelGGL((layout_place_kernel<kRanks, true>), dim3(1), dim3(kLayoutThreads), 0,
+                       stream, b, o);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(layout_hist_kernel<kRanks>, dim3(nblocks), dim3(kLayoutThreads), 0, stream,
                      b, o);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(layout_place_kernel<kRanks>, dim3(nblocks), dim3(kLayoutThreads), 0, stream,
-                     b, o);
+  hipLaunchKernelGGL((layout_place_kernel<kRanks, false>), dim3(nblocks), dim3(kLayoutThreads),
+                     0, stream, b, o);
   return hipGetLastError();
 }
 
