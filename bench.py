@@ -44,7 +44,7 @@ def mxfp8_bytes(T, H, k):
     return 2 * T * H + S * H + S * (H // 32) + 4 * S
 
 
-KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_kernel<TableRows>",
+KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_slots_kernel<TableRows>",
                 "dispatch_fp8": "dispatch_fp8_kernel<TableRows>", "combine": "combine_kernel<true>"}
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "traffic_deepseekv3.json")

@@ -63,6 +63,13 @@ hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, voi
                            void* d_scales, int64_t rows, int num_tokens, int topk, int hidden,
                            int max_blocks, hipStream_t stream);
 
+// bf16 dispatch for tables in which many slots are -1 (the rank-deduplicated
+// layout): one wavefront per (token, slice) loops over the slots, where
+// launch_dispatch gives every slot a wavefront of its own.
+hipError_t launch_dispatch_sparse(const void* d_x, const int32_t* d_pos, void* d_out, int64_t rows,
+                                  int num_tokens, int topk, int hidden, int max_blocks,
+                                  hipStream_t stream);
+
 // Fixed-capacity (decode-time) layout and dispatch in one launch: rows
 // [e*capacity, (e+1)*capacity) belong to expert e. Records d_pos [T, k],
 // d_counts [E] and d_status [4] (invalid, placed, T, dropped).
