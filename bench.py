@@ -44,6 +44,72 @@ def mxfp8_bytes(T, H, k):
     return 2 * T * H + S * H + S * (H // 32) + 4 * S
 
 
+class HipTimer:
+    """A HIP timing event created with hipEventDisableSystemFence.
+
+    A default event (torch.cuda.Event) records with a system-scope release
+    and acquire: the GPU writes back and invalidates its caches at every
+    record, which costs microseconds and slows the kernel that follows, so
+    the op between two such events looks slower than it runs. These events
+    only take timestamps on the launch stream. The functions come from the
+    HIP runtime the kernels library (and torch) already use, looked up
+    through the library's own handle.
+    """
+
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            from combine_moe_dispatch_02_amd import _lib
+            hip = _lib.load()
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ev = ctypes.c_void_p()
+        err = self._runtime().hipEventCreateWithFlags(ctypes.byref(self._ev),
+                                                     self.DISABLE_SYSTEM_FENCE)
+        if err != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {err}")
+
+    def record(self, stream):
+        err = self._runtime().hipEventRecord(self._ev, stream.cuda_stream)
+        if err != 0:
+            raise RuntimeError(f"hipEventRecord failed: {err}")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        err = self._runtime().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev)
+        if err != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {err}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and getattr(self, "_ev", None):
+            self._hip.hipEventDestroy(self._ev)
+
+
+def queue_ahead():
+    """Keep the GPU busy (a bounded spin of about 2 ms: torch's own sleep
+    kernel) while the host enqueues a timing loop, so that every event
+    records back to back on the GPU and no call's time includes host launch
+    latency. Without it a small op (a few us) is timed at the host's launch
+    rate."""
+    import torch
+    torch.cuda._sleep(4_000_000)
+
+
 KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_slots_kernel<TableRows>",
                 "dispatch_fp8": "dispatch_fp8_kernel<TableRows>", "combine": "combine_kernel<true>"}
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -125,6 +191,8 @@ def main():
     skip = {x for x in args.skip.split(",") if x}
     if not skip <= {"rank", "decode", "sweep", "others"}:
         ap.error(f"--skip takes rank, decode, sweep, others; got {args.skip}")
+    if args.steps < 1:
+        ap.error("--steps must be at least 1")
     if "sweep" in skip:
         args.workgroup_sweep = 0
     if args.gpus != 1:
@@ -183,15 +251,17 @@ def main():
             run_op(name)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps. Every `instrument_every`-th step (and the
-    # first) records HIP events on the launch stream at every op boundary (op i
-    # spans events i and i+1 of that step); the per-op times and the roofline
-    # come from those steps. Each event costs about 3 us of GPU time, so the
-    # other steps run without events and the wall time per step is not
-    # inflated by the timing itself.
+    # Timed region: exactly K steps. Every `instrument_every`-th step (steps
+    # every-1, 2*every-1, ...; the last step if K < every) records HIP events
+    # (HipTimer: timestamps without cache maintenance) on the launch stream at
+    # every op boundary (op i spans events i and i+1 of that step); the per-op
+    # times and the roofline come from those steps. Step 0 is never among
+    # them: it starts on an idle GPU, where an event would also time the
+    # host's launch latency. The other steps run without events, so the wall
+    # time per step carries as little timing overhead as possible.
     every = max(1, args.instrument_every)
-    instrumented = [i for i in range(args.steps) if i % every == 0]
-    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+    instrumented = [i for i in range(args.steps) if i % every == every - 1] or [args.steps - 1]
+    ev = {i: [HipTimer() for _ in range(len(ops) + 1)]
           for i in instrumented}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -227,8 +297,9 @@ def main():
     sustained = {}
     if args.sustained_iters > 0:
         for name in ops:
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            evs = [(HipTimer(), HipTimer())
                    for _ in range(args.sustained_iters)]
+            queue_ahead()
             for i in range(3 + args.sustained_iters):
                 cur["i"] = i % len(sets)
                 if i >= 3:
@@ -252,8 +323,9 @@ def main():
         bufs = [torch.empty(max(wbytes, 2 * half), dtype=torch.uint8, device=dev) for _ in range(3)]
         for label, moved, fn in (("copy_same_bytes", 2 * half, lambda b: b[half:2 * half].copy_(b[:half])),
                                  ("write_same_bytes", wbytes, lambda b: b[:wbytes].fill_(7))):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            evs = [(HipTimer(), HipTimer())
                    for _ in range(args.sustained_iters)]
+            queue_ahead()
             for i in range(3 + args.sustained_iters):
                 if i >= 3:
                     evs[i - 3][0].record(stream)
@@ -269,9 +341,10 @@ def main():
         for b in sets:
             b["mx_scales"] = torch.empty((S, H // 32), dtype=torch.uint8, device=dev)
         mx = mxfp8_bytes(T, H, k)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        evs = [(HipTimer(), HipTimer())
                for _ in range(args.sustained_iters)]
         h.layout(sets[0]["idx"])
+        queue_ahead()
         for i in range(3 + args.sustained_iters):
             b = sets[i % len(sets)]
             if i >= 3:
@@ -306,8 +379,9 @@ def main():
                                                               recv_idx=b["r_idx"], recv_w=b["r_w"]),
                  "combine_ranks": lambda b: h.combine_ranks(b["r_out"], out=b["c_out"])}
         for name, fn in calls.items():
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            evs = [(HipTimer(), HipTimer())
                    for _ in range(args.sustained_iters)]
+            queue_ahead()
             for i in range(3 + args.sustained_iters):
                 if i >= 3:
                     evs[i - 3][0].record(stream)
@@ -331,8 +405,9 @@ def main():
             h.set_max_workgroups(cap)
             row = {}
             for name in ("dispatch_bf16", "dispatch_fp8", "combine"):
-                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                evs = [(HipTimer(), HipTimer())
                        for _ in range(5)]
+                queue_ahead()
                 for i in range(7):
                     cur["i"] = i % len(sets)
                     if i >= 2:
@@ -348,8 +423,9 @@ def main():
 
     def sustained_us(fn, iters):
         """Median µs of fn(i) over back-to-back calls (3 untimed first)."""
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        evs = [(HipTimer(), HipTimer())
                for _ in range(iters)]
+        queue_ahead()
         for i in range(3 + iters):
             if i >= 3:
                 evs[i - 3][0].record(stream)
