@@ -337,6 +337,30 @@ def main():
             sustained[label] = {"bytes": moved, "us_median": round(float(np.median(us)), 2),
                                 "GBps": round(moved / (np.median(us) * 1e-6) / 1e9, 1)}
         del bufs
+        # Context: the two dispatches with x evicted from the last-level cache.
+        # Across the rotating sets x (2*T*H bytes per set) stays cache-resident:
+        # the dispatches' non-temporal row stores and combine's non-temporal
+        # loads do not displace it. Here every timed call follows a 1 GiB read
+        # sweep (a reduction; no dirty lines), outside its events.
+        sweep_src = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.zeros((), dtype=torch.float32, device=dev)
+        evicted = {}
+        for name in ("dispatch_bf16", "dispatch_fp8"):
+            evs = [(HipTimer(), HipTimer()) for _ in range(args.sustained_iters)]
+            for i in range(3 + args.sustained_iters):
+                cur["i"] = i % len(sets)
+                sink.copy_(sweep_src.amax())
+                if i >= 3:
+                    evs[i - 3][0].record(stream)
+                run_op(name)
+                if i >= 3:
+                    evs[i - 3][1].record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            evicted[name] = {"us_median": round(us, 2),
+                             "GBps": round(nbytes[name] / (us * 1e-6) / 1e9, 1)}
+        sustained["x_evicted"] = evicted
+        del sweep_src, sink
         # MXFP8 dispatch (32-channel blocks, E8M0 scales), same method.
         for b in sets:
             b["mx_scales"] = torch.empty((S, H // 32), dtype=torch.uint8, device=dev)

@@ -332,16 +332,22 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_kernel(
   }
 }
 
-// bf16 dispatch with one wavefront per slot: a workgroup is one (token,
-// 512-channel slice) item, and its W wavefronts (W = min(k, kSlotWaves))
-// take slots w, w + W, ... Every wavefront loads the same 1 KiB of x (one
-// HBM read; the other wavefronts of the workgroup find it in the CU's cache)
-// and stores it once per slot. Compared with one wavefront storing all k
-// rows, a wavefront issues one store instead of k, and the same scatter
-// reaches HBM about 3% faster (T=4096, H=7168, k=8); plain sequential
-// writes show the same effect more strongly (1 KiB per wavefront 73 us,
-// 8 KiB per wavefront 90 us for the same 470 MB).
+// bf16 dispatch with the slots spread over a workgroup: a workgroup is one
+// (token, 512-channel slice) item, and its W = min(ceil(k/2), kSlotWaves)
+// wavefronts take slots w, w + W, ... (two each at k = 8). Every wavefront
+// loads the same 1 KiB of x (one HBM read; the other wavefronts of the
+// workgroup find it in the cache) and stores it once per slot. A wavefront
+// that issues fewer stores lets the scatter reach HBM faster: plain
+// sequential writes of the same 470 MB take 73 us at one 1 KiB store per
+// wavefront and 90 us at eight. One slot per wavefront is faster still while
+// x is cache-resident (T=4096, H=7168: 90-92 vs 93-95 us) but 15-25% slower
+// than two when x comes from HBM (T=16384, H=4096: 282 vs 219 us; T=8192,
+// H=7168: 256 vs 205 us), where eight wavefronts wait on one cold load; two
+// slots per wavefront is the faster of the two designs or within 2% of it
+// at every shape measured, and beats one wavefront looping over all k slots
+// by 3-10% once x comes from HBM.
 constexpr int kSlotWaves = 8;
+constexpr int kSlotsPerWave = 2;
 
 template <class Rows>
 __global__ __launch_bounds__(64 * kSlotWaves) void dispatch_bf16_slots_kernel(
@@ -775,9 +781,11 @@ hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, voi
   u32x4* out = static_cast<u32x4*>(d_out);
   const TableRows tr{d_pos, topk, rows};
   if (dtype == MOE_DTYPE_BF16) {
-    // One workgroup of min(k, kSlotWaves) wavefronts per item; a cap keeps
-    // the wavefront count of max_blocks workgroups of kItemWaves.
-    const int waves = topk < kSlotWaves ? topk : kSlotWaves;
+    // One workgroup of min(ceil(k / kSlotsPerWave), kSlotWaves) wavefronts
+    // per item; a cap keeps the wavefront count of max_blocks workgroups of
+    // kItemWaves.
+    const int want = (topk + kSlotsPerWave - 1) / kSlotsPerWave;
+    const int waves = want < kSlotWaves ? want : kSlotWaves;
     int64_t blocks = int64_t(num_tokens) * slices;
     if (max_blocks > 0) {
       int64_t cap = int64_t(max_blocks) * kItemWaves / waves;

@@ -215,11 +215,11 @@ int moe_combine_ranks(moe_handle_t h, const void* d_y, int64_t y_rows, void* d_o
                       hipStream_t stream);
 
 /* Cap the dispatch and combine calls at the wavefronts of max_workgroups
- * workgroups of 4 (the standard bf16 dispatch, whose workgroups are one
- * wavefront per slot, min(k, 8) wide, launches 4 * max_workgroups / min(k, 8)
- * of them, at least one); 0 (the default) launches one workgroup per 4 work
- * items (bf16 dispatch: per item). With a cap, each wavefront loops over
- * several (token, column slice) items,
+ * workgroups of 4 (the standard bf16 dispatch, whose workgroups spread a
+ * token's slots over W = min(ceil(k/2), 8) wavefronts, launches
+ * 4 * max_workgroups / W of them, at least one); 0 (the default) launches one
+ * workgroup per 4 work items (bf16 dispatch: per item). With a cap, each
+ * wavefront loops over several (token, column slice) items,
  * so the work occupies fewer compute units and leaves the rest free for
  * kernels on other streams -- the pages' point that the exchange should fill
  * the link with few compute units (Hybrid-EP news item, "Efficiency
