@@ -7,15 +7,17 @@
 // ("MoE / Hybrid-EP Validation", "Communication path comparison" and "FP8
 // dispatch restriction").
 //
-// Work decomposition: every wavefront is an independent work item, one
-// (token, column slice) pair, and a workgroup is just kItemWaves such items.
-// The Hybrid-EP news item ("Technical Structure") describes each CUDA block
-// as an independent channel with no cross-block synchronisation; here the
-// independent unit is the 64-lane wavefront, which has no barrier at all.
-// A wavefront fetches the token's k row indices with scalar loads up front,
-// reads its slice of the token row from HBM once (16 bytes per lane, so 1 KiB
-// per wavefront for bf16), and writes it to the k destination rows with
-// 16-byte stores. No two wavefronts write the same bytes: no atomics.
+// Work decomposition: no workgroup waits for another. The Hybrid-EP news
+// item ("Technical Structure") describes each CUDA block as an independent
+// channel with no cross-block synchronisation; here the independent unit is
+// a (token, column slice) item. FP8/MXFP8 (and bf16 through the
+// rank-deduplicated table): one wavefront per item, kItemWaves items per
+// workgroup; the wavefront fetches the token's k row indices with scalar
+// loads, reads its slice of the token row once (16 bytes per lane) and
+// writes it to the k destination rows with 16-byte stores. Standard bf16:
+// one workgroup per item, the token's slots spread over its wavefronts
+// (dispatch_bf16_slots_kernel). No two wavefronts write the same bytes: no
+// atomics, and no barrier in either form.
 //
 // Row stores are non-temporal: each dispatched row is written once and its
 // next reader (the expert computation) is another kernel, so the rows stream
