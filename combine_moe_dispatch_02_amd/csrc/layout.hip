@@ -14,13 +14,15 @@
 //
 // Two launches, no grid-wide synchronisation:
 //   1. layout_hist_kernel   -- each workgroup counts the expert ids of its own
-//      chunk of 2048 slots into an LDS histogram and writes it out.
+//      chunk of 1024 slots into an LDS histogram and writes it out.
 //   2. layout_place_kernel  -- each workgroup sums the histograms column-wise
 //      (all workgroups for the expert totals, earlier ones for its own base),
 //      scans the totals over experts, then walks its chunk again in slot order
 //      and assigns rows. Workgroup 0 also publishes counts and offsets.
-// When all slots fit one chunk (2048, e.g. 256 tokens at top-8) the place
-// kernel alone does both: its own per-wavefront counts are the totals.
+// Up to 4096 slots (512 tokens at top-8) one workgroup of the place kernel
+// does both, each wavefront taking 128, 256 or 512 slots (as few as cover
+// them): its own per-wavefront counts are the totals. Beyond that,
+// workgroups of 1024 slots.
 //
 // Inside a wavefront, lanes that hold the same expert id find each other with
 // ceil(log2 E) ballots (one per id bit); the lowest lane of each group does
@@ -84,19 +86,19 @@ __device__ __forceinline__ int rank_of(const Buckets& b, int e) {
   return static_cast<int>((static_cast<uint32_t>(e) * b.rank_mul) >> 20);
 }
 
-// Buckets of this wavefront's kLayoutSteps 64-slot steps starting at `base`
-// (lane l of step s holds slot base + 64 s + l). Every lane must call it.
-template <bool kRanks>
+// Buckets of this wavefront's kSteps 64-slot steps starting at `base` (lane
+// l of step s holds slot base + 64 s + l). Every lane must call it.
+template <bool kRanks, int kSteps>
 __device__ __forceinline__ void load_buckets(const Buckets& b, int base, int lane,
-                                             int (&ids)[kLayoutSteps]) {
-  int raw[kLayoutSteps];
+                                             int (&ids)[kSteps]) {
+  int raw[kSteps];
 #pragma unroll
-  for (int s = 0; s < kLayoutSteps; ++s) {
+  for (int s = 0; s < kSteps; ++s) {
     const int slot = base + s * 64 + lane;
     raw[s] = slot < b.slots ? b.idx[slot] : -1;
   }
 #pragma unroll
-  for (int s = 0; s < kLayoutSteps; ++s) {
+  for (int s = 0; s < kSteps; ++s) {
     const int e = raw[s];
     const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(b.num_experts);
     if (!kRanks) {
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(Buckets b, 
   const int lane = tid & 63;
   const int base = blockIdx.x * kLayoutChunk + (tid >> 6) * (kLayoutSteps * 64);
   int ids[kLayoutSteps];
-  load_buckets<kRanks>(b, base, lane, ids);
+  load_buckets<kRanks, kLayoutSteps>(b, base, lane, ids);
 #pragma unroll
   for (int s = 0; s < kLayoutSteps; ++s) {
     const int e = ids[s];
@@ -154,8 +156,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(Buckets b, 
   for (int e = tid; e < b.nbuckets; e += kLayoutThreads) out[e] = s_hist[e];
 }
 
-// kSingle: one workgroup holds every slot; no histogram kernel ran before it.
-template <bool kRanks, bool kSingle>
+// kSteps: 64-slot steps per wavefront. kSingle: one workgroup holds every
+// slot (up to kLayoutThreads * kSteps); no histogram kernel ran before it.
+template <bool kRanks, int kSteps, bool kSingle>
 __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b, LayoutOut o) {
   // s_cur[w * E + e]: wavefront w's running row cursor for bucket e.
   __shared__ int32_t s_cur[kLayoutWaves * MOE_EP_MAX_EXPERTS];
@@ -175,9 +178,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
 
   // This wavefront's slot ids, loaded first so that their latency overlaps
   // the histogram reads below.
-  const int base = blockIdx.x * kLayoutChunk + wave * (kLayoutSteps * 64);
-  int ids[kLayoutSteps];
-  load_buckets<kRanks>(b, base, lane, ids);
+  const int base = blockIdx.x * (kLayoutThreads * kSteps) + wave * (kSteps * 64);
+  int ids[kSteps];
+  load_buckets<kRanks, kSteps>(b, base, lane, ids);
 
   // Column sums of the per-workgroup histograms: the bucket totals, and the
   // part that earlier workgroups (earlier slots) contribute.
@@ -195,10 +198,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
   __syncthreads();
 
   // Pass 1 over this workgroup's chunk: per-wavefront histograms.
-  uint64_t peers[kLayoutSteps];
+  uint64_t peers[kSteps];
   int32_t* my_cur = s_cur + wave * E;
 #pragma unroll
-  for (int s = 0; s < kLayoutSteps; ++s) {
+  for (int s = 0; s < kSteps; ++s) {
     const int e = ids[s];
     const bool valid = e >= 0;
     peers[s] = same_expert_lanes(e, valid, b.nbits);
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
   // Pass 2: rows in slot order. All lanes of a group read the cursor before
   // the leader advances it (LDS operations of one wavefront stay in order).
 #pragma unroll
-  for (int s = 0; s < kLayoutSteps; ++s) {
+  for (int s = 0; s < kSteps; ++s) {
     const int slot = base + s * 64 + lane;
     const int e = ids[s];
     int p = -1;
@@ -326,17 +329,24 @@ int bits_for(int n) {
 template <bool kRanks>
 hipError_t launch_pass(const Buckets& b, const LayoutOut& o, hipStream_t stream) {
   const int nblocks = layout_blocks(b.slots);
-  if (nblocks == 1) {
-    hipLaunchKernelGGL((layout_place_kernel<kRanks, true>), dim3(1), dim3(kLayoutThreads), 0,
-                       stream, b, o);
+  if (b.slots <= kLayoutSingleChunk) {   // one workgroup, as few steps as cover the slots
+    if (b.slots <= kLayoutThreads * 2)
+      hipLaunchKernelGGL((layout_place_kernel<kRanks, 2, true>), dim3(1), dim3(kLayoutThreads),
+                         0, stream, b, o);
+    else if (b.slots <= kLayoutThreads * 4)
+      hipLaunchKernelGGL((layout_place_kernel<kRanks, 4, true>), dim3(1), dim3(kLayoutThreads),
+                         0, stream, b, o);
+    else
+      hipLaunchKernelGGL((layout_place_kernel<kRanks, kLayoutSingleSteps, true>), dim3(1),
+                         dim3(kLayoutThreads), 0, stream, b, o);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(layout_hist_kernel<kRanks>, dim3(nblocks), dim3(kLayoutThreads), 0, stream,
                      b, o);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((layout_place_kernel<kRanks, false>), dim3(nblocks), dim3(kLayoutThreads),
-                     0, stream, b, o);
+  hipLaunchKernelGGL((layout_place_kernel<kRanks, kLayoutSteps, false>), dim3(nblocks),
+                     dim3(kLayoutThreads), 0, stream, b, o);
   return hipGetLastError();
 }
 

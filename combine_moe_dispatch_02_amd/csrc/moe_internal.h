@@ -13,8 +13,11 @@ namespace moe {
 // Layout kernels: one workgroup owns a contiguous chunk of slots.
 constexpr int kLayoutThreads = 512;                 // 8 wavefronts
 constexpr int kLayoutWaves = kLayoutThreads / 64;
-constexpr int kLayoutSteps = 4;                     // 64-slot steps per wavefront
-constexpr int kLayoutChunk = kLayoutThreads * kLayoutSteps;  // 2048 slots per workgroup
+constexpr int kLayoutSteps = 2;                     // 64-slot steps per wavefront
+constexpr int kLayoutChunk = kLayoutThreads * kLayoutSteps;  // 1024 slots per workgroup
+// Up to this many slots one workgroup lays out everything in one launch.
+constexpr int kLayoutSingleSteps = 8;
+constexpr int kLayoutSingleChunk = kLayoutThreads * kLayoutSingleSteps;  // 4096 slots
 
 inline int layout_blocks(int64_t slots) {
   int64_t b = (slots + kLayoutChunk - 1) / kLayoutChunk;

@@ -54,10 +54,10 @@ def test_workspace_bytes(lib):
     c = cfg(4096, 7168, 8, 256, 8)
     n = lib.moe_workspace_bytes(ctypes.byref(c))
     slots = 4096 * 8
-    # expert layout: pos + src_idx + 16 histograms of 256 experts; rank layout:
-    # slot_row + rank_pos [T, 8] + src [T * 8] + 16 histograms of 8 ranks; decode-time
-    # layout: pos [1024 * 8] + counts [256]; small arrays
-    need = (2 * 4 * slots + 16 * 256 * 4 + 4 * slots + 4 * 4096 * 8 + 4 * 4096 * 8 + 16 * 8 * 4
+    # expert layout: pos + src_idx + 32 histograms (one per 1024-slot workgroup) of 256
+    # experts; rank layout: slot_row + rank_pos [T, 8] + src [T * 8] + 32 histograms of 8
+    # ranks; decode-time layout: pos [1024 * 8] + counts [256]; small arrays
+    need = (2 * 4 * slots + 32 * 256 * 4 + 4 * slots + 4 * 4096 * 8 + 4 * 4096 * 8 + 32 * 8 * 4
             + 4 * 1024 * 8 + 4 * 256)
     assert need <= n < need + 16 * 1024
     assert n % 256 == 0
