@@ -100,6 +100,9 @@ class HipTimer:
             self._hip.hipEventDestroy(self._ev)
 
 
+_QUEUE_AHEAD_BUF = None
+
+
 def queue_ahead():
     """Keep the GPU busy (a bounded spin of about 2 ms: torch's own sleep
     kernel) while the host enqueues a timing loop, so that every event
@@ -107,7 +110,18 @@ def queue_ahead():
     latency. Without it a small op (a few us) is timed at the host's launch
     rate."""
     import torch
-    torch.cuda._sleep(4_000_000)
+    sleep = getattr(torch.cuda, "_sleep", None)
+    if sleep is not None:
+        sleep(4_000_000)
+        return
+    # Without torch's sleep kernel: about 2 ms of plain device writes instead
+    # (their dirty lines are written back during the first timed calls, which
+    # then read a little slower).
+    global _QUEUE_AHEAD_BUF
+    if _QUEUE_AHEAD_BUF is None:
+        _QUEUE_AHEAD_BUF = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for i in range(8):
+        _QUEUE_AHEAD_BUF.fill_(i)
 
 
 KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_slots_kernel<TableRows>",
