@@ -174,6 +174,23 @@ def test_large_token_count_layout():
     assert_layout_equal(got, ref, T, k)
 
 
+# Slot counts at the layout's workgroup boundaries: one workgroup with 2, 4 or
+# 8 steps of 64 slots per wavefront up to 1024 / 2048 / 4096 slots, then
+# workgroups of 1024 slots (a ragged last one included).
+BOUNDARY_SLOTS = (1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097, 5120, 8191)
+
+
+@pytest.mark.parametrize("slots", BOUNDARY_SLOTS)
+def test_layout_at_workgroup_boundaries(slots):
+    k = 1 if slots % 8 else 8
+    T = slots // k
+    for E, R, pattern, seed in ((256, 8, "random", 1), (16, 4, "invalid", 2), (64, 8, "const", 3)):
+        print(f"[boundary] slots={T * k} T={T} k={k} E={E} {pattern}", flush=True)
+        idx = edge_ids(T, k, E, pattern, seed=seed)
+        got = layout_on_gpu(Handle(T, 128, k, E, R), idx)
+        assert_layout_equal(got, oracle.layout(idx, E, R), T, k)
+
+
 def test_layout_reuse_with_fewer_tokens():
     """A handle sized for T_max serves a smaller batch after a larger one."""
     h = Handle(4096, 256, 8, 256, 8)

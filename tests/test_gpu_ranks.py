@@ -51,6 +51,19 @@ def check_rank_layout(h, idx, E, R):
     return ref
 
 
+@pytest.mark.parametrize("slots", (1024, 1025, 2048, 2049, 4096, 4097, 8191))
+def test_rank_layout_at_workgroup_boundaries(slots):
+    """Slot counts where the layout changes workgroup shape (one workgroup
+    with 2, 4 or 8 steps per wavefront, then workgroups of 1024 slots)."""
+    k = 1 if slots % 8 else 8
+    T = slots // k
+    E, R = 64, 8
+    rng = np.random.default_rng(slots)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    print(f"[rank boundary] slots={T * k} T={T} k={k}", flush=True)
+    check_rank_layout(Handle(T, 128, k, E, R), idx, E, R)
+
+
 @pytest.mark.parametrize("name", NAMES)
 def test_rank_layout_and_dispatch_match_oracle(name):
     wl = make_workload(name)
