@@ -25,7 +25,9 @@ inline int layout_blocks(int64_t slots) {
 }
 
 // Payload kernels: every wavefront is one independent work item, a
-// (token, column slice) pair; a workgroup is kItemWaves such items.
+// (token, column slice) pair; a workgroup is kItemWaves such items. (The
+// standard bf16 dispatch instead gives each item a workgroup whose
+// wavefronts share the item's slots; its cap keeps the same wavefront count.)
 constexpr int kItemWaves = 4;
 constexpr int kSlotBatch = 8;   // row indices fetched (and rows read) per batch
 
