@@ -10,10 +10,11 @@
 // scheduling.
 //
 // Work decomposition as in dispatch: every wavefront is one (token, 1 KiB
-// column slice) work item. It fetches the token's row indices and weights
-// with scalar loads, issues the 16-byte loads of up to 8 slot rows back to
-// back (8 independent reads in flight per lane), then accumulates them in
-// slot order and writes the bf16 slice with one 16-byte store per lane.
+// column slice) work item, two items to a workgroup. It fetches the token's
+// row indices and weights with scalar loads, issues the 16-byte loads of up
+// to 8 slot rows back to back (8 independent reads in flight per lane), then
+// accumulates them in slot order and writes the bf16 slice with one 16-byte
+// store per lane.
 //
 // Combine is the last reader of the expert outputs, so those rows are read
 // with non-temporal loads, and the token rows are written with non-temporal
@@ -58,13 +59,13 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], float w, const u32x4
 // reduction of the rank-deduplicated exchange, over the per-rank partial rows
 // of each token in ascending rank order.
 template <bool kWeighted>
-__global__ __launch_bounds__(64 * kItemWaves) void combine_kernel(
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(
     const u32x4* __restrict__ y, const float* __restrict__ w, const int32_t* __restrict__ pos,
     u32x4* __restrict__ out, int num_tokens, int topk, int nvec, int slices, int64_t rows) {
   const int lane = threadIdx.x & 63;
   const int nitems = num_tokens * slices;
-  for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
-       item += gridDim.x * kItemWaves) {
+  for (int item = blockIdx.x * kCombineWaves + wave_index(); item < nitems;
+       item += gridDim.x * kCombineWaves) {
     const int t = item / slices;
     const int v = (item - t * slices) * 64 + lane;
     const bool active = v < nvec;
@@ -132,9 +133,10 @@ hipError_t launch_combine(const void* d_y, int64_t rows, const float* d_w, const
   if (num_tokens == 0) return hipSuccess;
   const int nvec = hidden / 8;
   const int slices = (nvec + 63) / 64;
-  hipLaunchKernelGGL(combine_kernel<true>, item_grid(int64_t(num_tokens) * slices, max_blocks),
-                     dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_y), d_w, d_pos,
-                     static_cast<u32x4*>(d_out), num_tokens, topk, nvec, slices, rows);
+  hipLaunchKernelGGL(combine_kernel<true>,
+                     wave_grid(int64_t(num_tokens) * slices, kCombineWaves, max_blocks),
+                     dim3(64 * kCombineWaves), 0, stream, static_cast<const u32x4*>(d_y), d_w,
+                     d_pos, static_cast<u32x4*>(d_out), num_tokens, topk, nvec, slices, rows);
   return hipGetLastError();
 }
 
@@ -144,8 +146,9 @@ hipError_t launch_combine_ranks(const void* d_y, int64_t rows, const int32_t* d_
   if (num_tokens == 0) return hipSuccess;
   const int nvec = hidden / 8;
   const int slices = (nvec + 63) / 64;
-  hipLaunchKernelGGL(combine_kernel<false>, item_grid(int64_t(num_tokens) * slices, max_blocks),
-                     dim3(64 * kItemWaves), 0, stream, static_cast<const u32x4*>(d_y), nullptr,
+  hipLaunchKernelGGL(combine_kernel<false>,
+                     wave_grid(int64_t(num_tokens) * slices, kCombineWaves, max_blocks),
+                     dim3(64 * kCombineWaves), 0, stream, static_cast<const u32x4*>(d_y), nullptr,
                      d_rank_pos, static_cast<u32x4*>(d_out), num_tokens, num_ranks, nvec, slices,
                      rows);
   return hipGetLastError();

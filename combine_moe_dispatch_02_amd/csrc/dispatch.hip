@@ -16,8 +16,9 @@
 // loads, reads its slice of the token row once (16 bytes per lane) and
 // writes it to the k destination rows with 16-byte stores. Standard bf16:
 // one workgroup per item, the token's slots spread over its wavefronts
-// (dispatch_bf16_slots_kernel). No two wavefronts write the same bytes: no
-// atomics, and no barrier in either form.
+// (dispatch_bf16_slots_kernel), or under a cap below kSlotsFormMinCap
+// workgroups the one-wavefront form. No two wavefronts write the same bytes:
+// no atomics, and no barrier in either form.
 //
 // Row stores are non-temporal: each dispatched row is written once and its
 // next reader (the expert computation) is another kernel, so the rows stream
@@ -350,6 +351,13 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_kernel(
 // by 3-10% once x comes from HBM.
 constexpr int kSlotWaves = 8;
 constexpr int kSlotsPerWave = 2;
+// Under a workgroup cap the wavefronts are few, and the form above keeps one
+// item in flight per four of them; looping over all k slots in one wavefront
+// (dispatch_bf16_kernel) keeps four. Same-box A/B at T=4096, H=7168, k=8
+// (GB/s, slots form / loop, two runs): cap 16 247-248 / 602-603, 128
+// 1828-1834 / 4158-4181, 256 3423-3430 / 5565-5596, 512 5800-5935 /
+// 5570-5582, 1024 5556-5610 / 5466-5617. So the loop below 512 workgroups.
+constexpr int kSlotsFormMinCap = 512;
 
 template <class Rows>
 __global__ __launch_bounds__(64 * kSlotWaves) void dispatch_bf16_slots_kernel(
@@ -782,7 +790,13 @@ hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, voi
   const u32x4* x = static_cast<const u32x4*>(d_x);
   u32x4* out = static_cast<u32x4*>(d_out);
   const TableRows tr{d_pos, topk, rows};
-  if (dtype == MOE_DTYPE_BF16) {
+  if (dtype == MOE_DTYPE_BF16 && max_blocks > 0 && max_blocks < kSlotsFormMinCap &&
+      int64_t(max_blocks) * kItemWaves < int64_t(num_tokens) * slices) {
+    // Capped below kSlotsFormMinCap workgroups: each wavefront takes one item
+    // and all of its k slots.
+    hipLaunchKernelGGL(dispatch_bf16_kernel<TableRows>, grid, block, 0, stream, x, tr, out,
+                       num_tokens, hidden / 8, slices, payload);
+  } else if (dtype == MOE_DTYPE_BF16) {
     // One workgroup of min(ceil(k / kSlotsPerWave), kSlotWaves) wavefronts
     // per item; a cap keeps the wavefront count of max_blocks workgroups of
     // kItemWaves.

@@ -25,11 +25,17 @@ inline int layout_blocks(int64_t slots) {
 }
 
 // Payload kernels: every wavefront is one independent work item, a
-// (token, column slice) pair; a workgroup is kItemWaves such items. (The
-// standard bf16 dispatch instead gives each item a workgroup whose
-// wavefronts share the item's slots; its cap keeps the same wavefront count.)
+// (token, column slice) pair; a workgroup is kItemWaves such items (combine:
+// kCombineWaves). (The standard bf16 dispatch instead gives each item a
+// workgroup whose wavefronts share the item's slots.) A workgroup cap is
+// counted in workgroups of kItemWaves; every kernel keeps that wavefront count.
 constexpr int kItemWaves = 4;
 constexpr int kSlotBatch = 8;   // row indices fetched (and rows read) per batch
+// Combine's workgroups hold two items: same-box A/B at T=4096, H=7168,
+// k=8 (two runs each, back to back over rotating buffers), combine 91.8 and
+// 92.6 us at four wavefronts per workgroup, 89.1 and 89.1 at two, 88.9 and
+// 89.9 at one.
+constexpr int kCombineWaves = 2;
 
 // Device views of the workspace regions.
 struct LayoutArrays {
@@ -149,6 +155,19 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 inline dim3 item_grid(int64_t num_items, int max_blocks) {
   int64_t blocks = (num_items + kItemWaves - 1) / kItemWaves;
   if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
+  return dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks));
+}
+
+// Grid for num_items wavefront work items in workgroups of `waves`
+// wavefronts. A cap of max_blocks (> 0) workgroups of kItemWaves keeps its
+// wavefront count: at most max_blocks * kItemWaves / waves workgroups.
+inline dim3 wave_grid(int64_t num_items, int waves, int max_blocks) {
+  int64_t blocks = (num_items + waves - 1) / waves;
+  if (max_blocks > 0) {
+    int64_t cap = int64_t(max_blocks) * kItemWaves / waves;
+    if (cap < 1) cap = 1;
+    if (blocks > cap) blocks = cap;
+  }
   return dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks));
 }
 

@@ -343,9 +343,14 @@ def test_fp8_pipeline_round_trip():
     assert np.all(np.abs(g - x) <= (2.0 ** -4 + 2.0 ** -7) * np.abs(x) + 2.0 ** -9 * s_tok + 1e-6)
 
 
-@pytest.mark.parametrize("cap", [1, 7, 64, 300])
+@pytest.mark.parametrize("cap", [1, 7, 64, 300, 511, 512, 700])
 def test_workgroup_cap_gives_identical_results(cap):
-    """Capping the grid only changes how many items each wavefront loops over."""
+    """Capping the grid only changes how many items each wavefront loops over.
+
+    The bf16 dispatch changes form at a cap of 512 workgroups (one wavefront
+    per item with all k slots below it, the slots spread over a workgroup
+    from it on); 600 tokens x 14 slices keep every cap here below the item
+    count, so both forms loop."""
     wl = make_workload("deepseekv3", tokens=600)
     s = wl.shape
     h = handle(s)
