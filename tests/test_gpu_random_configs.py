@@ -4,7 +4,8 @@ Each case draws T, H, k, E, R, an id pattern (uniform, skewed, duplicates,
 invalid ids) and a fixed-capacity C, then checks the layout, bf16 / FP8 /
 MXFP8 dispatch, combine, the rank-deduplicated exchange and the decode-time
 path to the same bars as the dedicated tests (bit-exact, combine within the
-combine tolerance). The draws are fixed by the case seed.
+combine tolerance), and reruns the dispatches and combine under a workgroup
+cap, which must give the same bits. The draws are fixed by the case seed.
 """
 import numpy as np
 import pytest
@@ -41,7 +42,10 @@ def draw_case(seed):
                             np.exp2(rng.integers(-8, 8, size=(T, 1)))).astype(np.float32))
     w = rng.uniform(-1, 1, size=(T, k)).astype(np.float32)
     C = int(rng.integers(1, max(2, (T * k) // E + 3)))
-    return dict(T=T, H=H, k=k, E=E, R=R, pattern=pattern, idx=idx.astype(np.int32), x=x, w=w, C=C)
+    # drawn last, so the draws above are those of the uncapped sweep
+    cap = int(rng.choice([1, 3, 17, 100, 511, 512, 700]))
+    return dict(T=T, H=H, k=k, E=E, R=R, pattern=pattern, idx=idx.astype(np.int32), x=x, w=w, C=C,
+                cap=cap)
 
 
 @pytest.mark.parametrize("seed", range(30))
@@ -49,7 +53,8 @@ def test_random_config(seed):
     c = draw_case(seed)
     T, H, k, E, R, C = c["T"], c["H"], c["k"], c["E"], c["R"], c["C"]
     idx, x, w = c["idx"], c["x"], c["w"]
-    print(f"[random {seed}] T={T} H={H} k={k} E={E} R={R} C={C} {c['pattern']}", flush=True)
+    print(f"[random {seed}] T={T} H={H} k={k} E={E} R={R} C={C} cap={c['cap']} {c['pattern']}",
+          flush=True)
     h = Handle(T, H, k, E, R)
     # standard layout and dispatches
     got = layout_on_gpu(h, idx)
@@ -57,20 +62,31 @@ def test_random_config(seed):
     assert_layout_equal(got, ref, T, k)
     n = int(ref["offsets_e"][-1])
     dx = dev_bf16(x)
-    assert np.array_equal(host_bits(h.dispatch(dx))[:n], oracle.dispatch_bf16(x, ref["pos"])[:n])
+    d16 = host_bits(h.dispatch(dx))
+    assert np.array_equal(d16[:n], oracle.dispatch_bf16(x, ref["pos"])[:n])
     q, s = h.dispatch(dx, fp8=True)
     rq, rs = oracle.dispatch_fp8(x, ref["pos"])
-    assert np.array_equal(host_bits(q)[:n], rq[:n])
-    assert np.array_equal(host_bits(s)[:n].view(np.uint32), rs[:n].view(np.uint32))
+    q8, s8 = host_bits(q), host_bits(s)
+    assert np.array_equal(q8[:n], rq[:n])
+    assert np.array_equal(s8[:n].view(np.uint32), rs[:n].view(np.uint32))
     q, s = h.dispatch(dx, mxfp8=True)
     rq, rs = oracle.dispatch_mxfp8(x, ref["pos"])
     assert np.array_equal(host_bits(q)[:n], rq[:n])
     assert np.array_equal(host_bits(s)[:n], rs[:n])
     # combine of independent expert outputs
     y = make_expert_outputs(T * k, H, seed=seed)
-    comb = host_bits(h.combine(dev_bf16(y), dev_f32(w)))
+    dy, dw = dev_bf16(y), dev_f32(w)
+    comb = host_bits(h.combine(dy, dw))
     want, mag = oracle.combine(y, w, ref["pos"], return_magnitude=True)
     assert_combine_close(comb, want, mag, k)
+    # the same calls under a workgroup cap: only the looping changes
+    h.set_max_workgroups(c["cap"])
+    capped = [host_bits(h.dispatch(dx)), *map(host_bits, h.dispatch(dx, fp8=True)),
+              host_bits(h.combine(dy, dw))]
+    h.set_max_workgroups(0)
+    assert np.array_equal(capped[0][:n], d16[:n])
+    assert np.array_equal(capped[1][:n], q8[:n]) and np.array_equal(capped[2][:n], s8[:n])
+    assert np.array_equal(capped[3], comb)
     # rank-deduplicated exchange
     h.rank_layout(dev_i32(idx))
     rl = oracle.rank_layout(idx, E, R)
