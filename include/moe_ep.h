@@ -215,10 +215,12 @@ int moe_combine_ranks(moe_handle_t h, const void* d_y, int64_t y_rows, void* d_o
                       hipStream_t stream);
 
 /* Cap the dispatch and combine calls at the wavefronts of max_workgroups
- * workgroups of 4 (the standard bf16 dispatch, whose workgroups spread a
- * token's slots over W = min(ceil(k/2), 8) wavefronts, launches
- * 4 * max_workgroups / W of them, at least one); 0 (the default) launches one
- * workgroup per 4 work items (bf16 dispatch: per item). With a cap, each
+ * workgroups of 4 (combine launches 2 * max_workgroups workgroups of 2; the
+ * standard bf16 dispatch, from 512 workgroups on, 4 * max_workgroups / W
+ * workgroups that spread a token's slots over W = min(ceil(k/2), 8)
+ * wavefronts, at least one, and below 512 one wavefront per item with all k
+ * slots); 0 (the default) launches one wavefront per (token, column slice)
+ * item (bf16 dispatch: one workgroup per item). With a cap, each
  * wavefront loops over several (token, column slice) items,
  * so the work occupies fewer compute units and leaves the rest free for
  * kernels on other streams -- the pages' point that the exchange should fill
