@@ -57,6 +57,42 @@ def _ptr(t: torch.Tensor | None, dtype, name: str, device=None) -> int | None:
     return t.data_ptr()
 
 
+# Configuration of every handle this module created, so that the calls below
+# can check tensor shapes against it: the library sees only pointers, and a
+# tensor smaller than the configuration implies would be read or written out
+# of bounds on the GPU.
+_CONFIGS: dict[int, MoeConfig] = {}
+
+
+def _matrix(t: torch.Tensor | None, name: str, cols: int, min_rows: int = 0) -> None:
+    if t is None:
+        return
+    if t.dim() != 2 or t.shape[1] != cols:
+        raise ValueError(f"{name} must be a [rows, {cols}] matrix, got shape {tuple(t.shape)}")
+    if t.shape[0] < min_rows:
+        raise ValueError(f"{name} has {t.shape[0]} rows; this call uses {min_rows}")
+
+
+def _tokens(h: int, view_fn, view_type) -> int | None:
+    """num_tokens of the handle's current layout of that kind, or None if it has none."""
+    v = view_type()
+    if view_fn(ctypes.c_void_p(h), ctypes.byref(v)) != _lib.MOE_OK:
+        return None
+    return int(v.num_tokens)
+
+
+def _check_payload(cfg: MoeConfig, tokens: int | None, x, dtype, out, scales) -> None:
+    _matrix(x, "x", cfg.hidden, tokens or 0)
+    _matrix(out, "out", cfg.hidden)
+    if out is None:
+        return
+    # a hidden size the quantised dtypes do not support is the library's error to report
+    if dtype == MOE_DTYPE_FP8_E4M3 and cfg.hidden % MOE_EP_FP8_BLOCK == 0:
+        _matrix(scales, "scales", cfg.hidden // MOE_EP_FP8_BLOCK, out.shape[0])
+    elif dtype == MOE_DTYPE_MXFP8_E4M3 and cfg.hidden % MOE_EP_FP8_BLOCK == 0:
+        _matrix(scales, "scales", cfg.hidden // MOE_MX_BLOCK, out.shape[0])
+
+
 def moe_workspace_bytes(max_tokens, hidden, topk, num_experts, num_ranks) -> int:
     lib = _lib.load()
     cfg = _config(max_tokens, hidden, topk, num_experts, num_ranks)
@@ -73,10 +109,12 @@ def moe_handle_create(max_tokens, hidden, topk, num_experts, num_ranks,
     h = ctypes.c_void_p()
     _lib.check(lib.moe_handle_create(ctypes.byref(cfg), ctypes.c_void_p(workspace_ptr),
                                      workspace_bytes, ctypes.byref(h)))
+    _CONFIGS[int(h.value)] = cfg
     return int(h.value)
 
 
 def moe_handle_destroy(h: int) -> None:
+    _CONFIGS.pop(int(h or 0), None)
     _lib.load().moe_handle_destroy(ctypes.c_void_p(h))
 
 
@@ -84,6 +122,9 @@ def moe_dispatch_layout(h: int, topk_idx: torch.Tensor, stream=None) -> None:
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [num_tokens, topk]")
     p = _ptr(topk_idx, torch.int32, "topk_idx")
+    cfg = _CONFIGS.get(h)
+    if cfg is not None:
+        _matrix(topk_idx, "topk_idx", cfg.topk)
     _lib.check(_lib.load().moe_dispatch_layout(ctypes.c_void_p(h), ctypes.c_void_p(p),
                                                topk_idx.shape[0], _stream(stream, topk_idx.device)))
 
@@ -108,6 +149,10 @@ def _payload_ptrs(x, dtype, out, scales):
 def moe_dispatch(h: int, x: torch.Tensor, dtype: int, out: torch.Tensor,
                  scales: torch.Tensor | None = None, stream=None) -> None:
     px, po, ps = _payload_ptrs(x, dtype, out, scales)
+    cfg = _CONFIGS.get(h)
+    if cfg is not None:
+        lib = _lib.load()
+        _check_payload(cfg, _tokens(h, lib.moe_layout_view, MoeLayoutView), x, dtype, out, scales)
     _lib.check(_lib.load().moe_dispatch(ctypes.c_void_p(h), ctypes.c_void_p(px), int(dtype),
                                         ctypes.c_void_p(po), ctypes.c_void_p(ps),
                                         out.shape[0], _stream(stream, x.device)))
@@ -117,6 +162,12 @@ def moe_combine(h: int, y: torch.Tensor, w: torch.Tensor, out: torch.Tensor, str
     py = _ptr(y, torch.bfloat16, "y")
     pw = _ptr(w, torch.float32, "w")
     po = _ptr(out, torch.bfloat16, "out")
+    cfg = _CONFIGS.get(h)
+    if cfg is not None:
+        tokens = _tokens(h, _lib.load().moe_layout_view, MoeLayoutView) or 0
+        _matrix(y, "y", cfg.hidden)
+        _matrix(w, "w", cfg.topk, tokens)
+        _matrix(out, "out", cfg.hidden, tokens)
     _lib.check(_lib.load().moe_combine(ctypes.c_void_p(h), ctypes.c_void_p(py), y.shape[0],
                                        ctypes.c_void_p(pw), ctypes.c_void_p(po),
                                        _stream(stream, y.device)))
@@ -126,6 +177,9 @@ def moe_rank_layout(h: int, topk_idx: torch.Tensor, stream=None) -> None:
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [num_tokens, topk]")
     p = _ptr(topk_idx, torch.int32, "topk_idx")
+    cfg = _CONFIGS.get(h)
+    if cfg is not None:
+        _matrix(topk_idx, "topk_idx", cfg.topk)
     _lib.check(_lib.load().moe_rank_layout(ctypes.c_void_p(h), ctypes.c_void_p(p),
                                            topk_idx.shape[0], _stream(stream, topk_idx.device)))
 
@@ -142,6 +196,15 @@ def moe_dispatch_ranks(h: int, x: torch.Tensor, topk_idx: torch.Tensor, w: torch
     args = [_ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int32, "topk_idx"),
             _ptr(w, torch.float32, "w"), _ptr(out, torch.bfloat16, "out"),
             _ptr(recv_idx, torch.int32, "recv_idx"), _ptr(recv_w, torch.float32, "recv_w")]
+    cfg = _CONFIGS.get(h)
+    if cfg is not None:
+        tokens = _tokens(h, _lib.load().moe_rank_layout_view, MoeRankLayoutView) or 0
+        _matrix(x, "x", cfg.hidden, tokens)
+        _matrix(topk_idx, "topk_idx", cfg.topk, tokens)
+        _matrix(w, "w", cfg.topk, tokens)
+        _matrix(out, "out", cfg.hidden)
+        _matrix(recv_idx, "recv_idx", cfg.topk, out.shape[0])
+        _matrix(recv_w, "recv_w", cfg.topk, out.shape[0])
     _lib.check(_lib.load().moe_dispatch_ranks(ctypes.c_void_p(h), *[ctypes.c_void_p(a) for a in args],
                                               out.shape[0], _stream(stream, x.device)))
 
@@ -149,6 +212,11 @@ def moe_dispatch_ranks(h: int, x: torch.Tensor, topk_idx: torch.Tensor, w: torch
 def moe_combine_ranks(h: int, y: torch.Tensor, out: torch.Tensor, stream=None) -> None:
     py = _ptr(y, torch.bfloat16, "y")
     po = _ptr(out, torch.bfloat16, "out")
+    cfg = _CONFIGS.get(h)
+    if cfg is not None:
+        tokens = _tokens(h, _lib.load().moe_rank_layout_view, MoeRankLayoutView) or 0
+        _matrix(y, "y", cfg.hidden)
+        _matrix(out, "out", cfg.hidden, tokens)
     _lib.check(_lib.load().moe_combine_ranks(ctypes.c_void_p(h), ctypes.c_void_p(py), y.shape[0],
                                              ctypes.c_void_p(po), _stream(stream, y.device)))
 
@@ -162,6 +230,11 @@ def moe_route(h: int, logits: torch.Tensor, score: int, topk_idx: torch.Tensor,
     pl = _ptr(logits, torch.float32, "logits")
     pi = _ptr(topk_idx, torch.int32, "topk_idx")
     pw = _ptr(topk_w, torch.float32, "topk_w")
+    cfg = _CONFIGS.get(h)
+    if cfg is not None:
+        _matrix(logits, "logits", cfg.num_experts)
+        _matrix(topk_idx, "topk_idx", cfg.topk, logits.shape[0])
+        _matrix(topk_w, "topk_w", cfg.topk, logits.shape[0])
     _lib.check(_lib.load().moe_route(ctypes.c_void_p(h), ctypes.c_void_p(pl), int(logits.shape[0]),
                                      int(score), ctypes.c_void_p(pi), ctypes.c_void_p(pw),
                                      _stream(stream, logits.device)))
@@ -171,6 +244,10 @@ def moe_layout_dispatch(h: int, topk_idx: torch.Tensor, x: torch.Tensor, dtype: 
                         out: torch.Tensor, scales: torch.Tensor | None, stream=None) -> None:
     pi = _ptr(topk_idx, torch.int32, "topk_idx")
     px, po, ps = _payload_ptrs(x, dtype, out, scales)
+    cfg = _CONFIGS.get(h)
+    if cfg is not None:
+        _matrix(topk_idx, "topk_idx", cfg.topk)
+        _check_payload(cfg, topk_idx.shape[0], x, dtype, out, scales)
     _lib.check(_lib.load().moe_layout_dispatch(
         ctypes.c_void_p(h), ctypes.c_void_p(pi), int(topk_idx.shape[0]), ctypes.c_void_p(px),
         int(dtype), ctypes.c_void_p(po), ctypes.c_void_p(ps), out.shape[0],
@@ -181,6 +258,10 @@ def moe_ll_dispatch(h: int, topk_idx: torch.Tensor, capacity: int, x: torch.Tens
                     out: torch.Tensor, scales: torch.Tensor | None, stream=None) -> None:
     pi = _ptr(topk_idx, torch.int32, "topk_idx")
     px, po, ps = _payload_ptrs(x, dtype, out, scales)
+    cfg = _CONFIGS.get(h)
+    if cfg is not None:
+        _matrix(topk_idx, "topk_idx", cfg.topk)
+        _check_payload(cfg, topk_idx.shape[0], x, dtype, out, scales)
     _lib.check(_lib.load().moe_ll_dispatch(
         ctypes.c_void_p(h), ctypes.c_void_p(pi), int(topk_idx.shape[0]), int(capacity),
         ctypes.c_void_p(px), int(dtype), ctypes.c_void_p(po), ctypes.c_void_p(ps), out.shape[0],
@@ -198,6 +279,12 @@ def moe_ll_combine(h: int, y: torch.Tensor, w: torch.Tensor, out: torch.Tensor,
     py = _ptr(y, torch.bfloat16, "y")
     pw = _ptr(w, torch.float32, "w")
     po = _ptr(out, torch.bfloat16, "out")
+    cfg = _CONFIGS.get(h)
+    if cfg is not None:
+        tokens = _tokens(h, _lib.load().moe_ll_view, MoeLlView) or 0
+        _matrix(y, "y", cfg.hidden)
+        _matrix(w, "w", cfg.topk, tokens)
+        _matrix(out, "out", cfg.hidden, tokens)
     _lib.check(_lib.load().moe_ll_combine(ctypes.c_void_p(h), ctypes.c_void_p(py), y.shape[0],
                                           ctypes.c_void_p(pw), ctypes.c_void_p(po),
                                           _stream(stream, y.device)))
@@ -226,6 +313,7 @@ class Handle:
         self.h = moe_handle_create(max_tokens, hidden, topk, num_experts, num_ranks,
                                    self.workspace.data_ptr(), nbytes)
         self._destroy = _lib.load().moe_handle_destroy   # kept for use at interpreter exit
+        self._configs = _CONFIGS                         # likewise
         self.num_tokens = None
         self.rank_num_tokens = None
         self.ll_num_tokens = None
@@ -233,6 +321,7 @@ class Handle:
     def __del__(self):
         h = getattr(self, "h", None)
         if h:
+            self._configs.pop(h, None)
             self._destroy(ctypes.c_void_p(h))
             self.h = None
 

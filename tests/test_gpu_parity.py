@@ -431,3 +431,57 @@ def test_host_errors_enqueue_nothing():
     with pytest.raises(MoeError, match="capacity"):
         h.combine(small, dev_f32(wl.topk_w))
     torch.cuda.synchronize()
+
+
+def test_binding_rejects_mis_shaped_tensors():
+    """The library sees only pointers; the binding refuses tensors whose shape
+    does not match the handle's configuration (which the kernels would read or
+    write out of bounds), before any call reaches the GPU."""
+    wl = make_workload("tiny")
+    s = wl.shape
+    T, H, k, E = s.tokens, s.hidden, s.topk, s.experts
+    S = T * k
+    h = handle(s)
+    idx, w, x = dev_i32(wl.topk_idx), dev_f32(wl.topk_w), dev_bf16(wl.x_bits)
+
+    def empty(shape, dtype):
+        return torch.empty(shape, dtype=dtype, device="cuda")
+
+    bf, u8, f32, i32 = torch.bfloat16, torch.uint8, torch.float32, torch.int32
+    with pytest.raises(ValueError, match="topk_idx"):
+        h.layout(empty((T, k + 1), i32))
+    with pytest.raises(ValueError, match="topk_idx"):
+        h.rank_layout(empty((T, k + 1), i32))
+    h.layout(idx)
+    h.rank_layout(idx)
+    bad = [
+        lambda: h.dispatch(empty((T - 1, H), bf)),                       # x: too few tokens
+        lambda: h.dispatch(empty((T, H - 8), bf)),                       # x: wrong width
+        lambda: h.dispatch(x, out=empty((S, H - 8), bf)),
+        lambda: h.dispatch(x, fp8=True, scales=empty((S, H // 128 - 1), f32)),
+        lambda: h.dispatch(x, fp8=True, scales=empty((S - 1, H // 128), f32)),
+        lambda: h.dispatch(x, mxfp8=True, scales=empty((S, H // 32 - 1), u8)),
+        lambda: h.combine(empty((S, H - 8), bf), w),
+        lambda: h.combine(empty((S, H), bf), empty((T, k - 1), f32)),
+        lambda: h.combine(empty((S, H), bf), empty((T - 1, k), f32)),
+        lambda: h.combine(empty((S, H), bf), w, out=empty((T - 1, H), bf)),
+        lambda: h.route(empty((T, E - 1), f32)),
+        lambda: h.route(empty((T, E), f32), topk_w=empty((T - 1, k), f32)),
+        lambda: h.dispatch_ranks(x, idx, empty((T, k - 1), f32)),
+        lambda: h.dispatch_ranks(x, idx, w, recv_idx=empty((h.rank_capacity - 1, k), i32)),
+        lambda: h.combine_ranks(empty((h.rank_capacity, H), bf), out=empty((T - 1, H), bf)),
+        lambda: h.layout_dispatch(empty((T, k - 1), i32), x),
+        lambda: h.ll_dispatch(idx, empty((T - 1, H), bf), 8),
+        lambda: h.ll_dispatch(idx, x, 8, "fp8", scales=empty((E * 8 - 1, H // 128), f32)),
+    ]
+    for call in bad:
+        with pytest.raises(ValueError):
+            call()
+    h.ll_dispatch(idx, x, 8)
+    with pytest.raises(ValueError, match="w"):
+        h.ll_combine(empty((E * 8, H), bf), empty((T - 1, k), f32))
+    # nothing above reached the GPU: the handle's layout still gives the oracle's rows
+    got = h.dispatch(x)
+    torch.cuda.synchronize()
+    ref = oracle.layout(wl.topk_idx, E, s.ranks)
+    assert np.array_equal(host_bits(got), oracle.dispatch_bf16(wl.x_bits, ref["pos"]))
