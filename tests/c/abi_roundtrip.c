@@ -1,5 +1,8 @@
 /* Plain-C use of the library's C ABI (no Python, no torch): layout, bf16
- * dispatch and combine with identity experts, plus one host-side error.
+ * dispatch and combine with identity experts, plus one host-side error. The
+ * round trip runs uncapped and under two workgroup caps (moe_set_max_workgroups:
+ * 7 takes the bf16 dispatch's one-wavefront-per-item form, 600 its
+ * slot-spread form; both loop over items).
  *
  * With weights of exactly 1/k, combine(dispatch(x)) rounds back to x bit for
  * bit (the fp32 sum of k copies of x/k is exact), except that -0 comes back
@@ -89,35 +92,43 @@ int main(void) {
     fprintf(stderr, "short output buffer was not refused\n");
     return 5;
   }
-  CHECK_MOE(moe_dispatch(h, d_x, MOE_DTYPE_BF16, d_rows, NULL, (int64_t)T * K, stream));
-  CHECK_MOE(moe_combine(h, d_rows, (int64_t)T * K, d_w, d_out, stream));
+  const int32_t caps[3] = {0, 7, 600};
+  for (int c = 0; c < 3; ++c) {
+    CHECK_HIP(hipMemsetAsync(d_rows, 0xFF, sizeof(uint16_t) * (size_t)T * K * H, stream));
+    CHECK_HIP(hipMemsetAsync(d_out, 0xFF, sizeof(uint16_t) * T * H, stream));
+    CHECK_MOE(moe_set_max_workgroups(h, caps[c]));
+    CHECK_MOE(moe_dispatch(h, d_x, MOE_DTYPE_BF16, d_rows, NULL, (int64_t)T * K, stream));
+    CHECK_MOE(moe_combine(h, d_rows, (int64_t)T * K, d_w, d_out, stream));
 
-  moe_layout_view_t view;
-  CHECK_MOE(moe_layout_view(h, &view));
-  CHECK_HIP(hipStreamSynchronize(stream));
-  CHECK_HIP(hipMemcpy(counts, view.counts_e, sizeof(int32_t) * E, hipMemcpyDeviceToHost));
-  CHECK_HIP(hipMemcpy(out, d_out, sizeof(uint16_t) * T * H, hipMemcpyDeviceToHost));
+    moe_layout_view_t view;
+    CHECK_MOE(moe_layout_view(h, &view));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    CHECK_HIP(hipMemcpy(counts, view.counts_e, sizeof(int32_t) * E, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(out, d_out, sizeof(uint16_t) * T * H, hipMemcpyDeviceToHost));
 
-  long total = 0;
-  for (int e = 0; e < E; ++e) total += counts[e];
-  if (total != (long)T * K) {
-    fprintf(stderr, "counts sum to %ld, expected %d\n", total, T * K);
-    return 6;
-  }
-  long bad = 0;
-  for (int i = 0; i < T * H; ++i) {
-    const uint16_t want = x[i] == 0x8000u ? 0 : x[i];
-    if (out[i] != want) ++bad;
-  }
-  if (bad) {
-    fprintf(stderr, "%ld elements differ after the round trip\n", bad);
-    return 7;
+    long total = 0;
+    for (int e = 0; e < E; ++e) total += counts[e];
+    if (total != (long)T * K) {
+      fprintf(stderr, "counts sum to %ld, expected %d\n", total, T * K);
+      return 6;
+    }
+    long bad = 0;
+    for (int i = 0; i < T * H; ++i) {
+      const uint16_t want = x[i] == 0x8000u ? 0 : x[i];
+      if (out[i] != want) ++bad;
+    }
+    if (bad) {
+      fprintf(stderr, "%ld elements differ after the round trip (workgroup cap %d)\n", bad,
+              caps[c]);
+      return 7;
+    }
   }
 
   moe_handle_destroy(h);
   CHECK_HIP(hipStreamDestroy(stream));
   hipFree(d_ws); hipFree(d_ids); hipFree(d_w); hipFree(d_x); hipFree(d_rows); hipFree(d_out);
   free(ids); free(w); free(x); free(out); free(counts);
-  printf("abi_roundtrip ok: %d tokens, top-%d of %d experts, hidden %d\n", T, K, E, H);
+  printf("abi_roundtrip ok: %d tokens, top-%d of %d experts, hidden %d, workgroup caps 0/7/600\n",
+         T, K, E, H);
   return 0;
 }
