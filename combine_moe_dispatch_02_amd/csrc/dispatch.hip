@@ -123,15 +123,21 @@ __device__ __forceinline__ uint32_t pack_e4m3(float a, float b, float c, float d
   return static_cast<uint32_t>(w);
 }
 
-// FP8 E4M3 quantisation of one lane's 16 channels (unit u of the row at src;
-// 8 consecutive lanes form a 128-channel block): codes q and the block scale.
-__device__ __forceinline__ void quantize_fp8(const u32x4* __restrict__ src, int u, bool active,
-                                             u32x4& q, float& scale) {
-  u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+// Lane u's 16 channels of the row at src (zeros for an inactive lane).
+__device__ __forceinline__ void load_lane16(const u32x4* __restrict__ src, int u, bool active,
+                                            u32x4& a, u32x4& b) {
+  a = {0u, 0u, 0u, 0u};
+  b = {0u, 0u, 0u, 0u};
   if (active) {
     a = src[2 * u];
     b = src[2 * u + 1];
   }
+}
+
+// FP8 E4M3 quantisation of one lane's 16 channels a, b (unit u of a row; 8
+// consecutive lanes form a 128-channel block): codes q and the block scale.
+__device__ __forceinline__ void quantize_fp8(const u32x4& a, const u32x4& b, u32x4& q,
+                                             float& scale) {
   float f[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
                  bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
                  bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
@@ -153,16 +159,19 @@ __device__ __forceinline__ void quantize_fp8(const u32x4* __restrict__ src, int 
   q.w = pack_e4m3(f[12], f[13], f[14], f[15]);
 }
 
+// The same, loading unit u of the row at src first.
+__device__ __forceinline__ void quantize_fp8(const u32x4* __restrict__ src, int u, bool active,
+                                             u32x4& q, float& scale) {
+  u32x4 a, b;
+  load_lane16(src, u, active, a, b);
+  quantize_fp8(a, b, q, scale);
+}
+
 // MXFP8 quantisation of one lane's 16 channels (a lane pair is one 32-channel
 // block): codes q and, in lanes 8i, the dword of four E8M0 codes of blocks
 // u/2 .. u/2+3.
-__device__ __forceinline__ void quantize_mxfp8(const u32x4* __restrict__ src, int u, int lane,
-                                               bool active, u32x4& q, uint32_t& word) {
-  u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-  if (active) {
-    a = src[2 * u];
-    b = src[2 * u + 1];
-  }
+__device__ __forceinline__ void quantize_mxfp8(const u32x4& a, const u32x4& b, int lane,
+                                               u32x4& q, uint32_t& word) {
   float f[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
                  bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
                  bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
@@ -191,6 +200,14 @@ __device__ __forceinline__ void quantize_mxfp8(const u32x4* __restrict__ src, in
   const uint32_t c2 = __shfl(code, lane + 4, 64);
   const uint32_t c3 = __shfl(code, lane + 6, 64);
   word = code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+}
+
+// The same, loading unit u of the row at src first.
+__device__ __forceinline__ void quantize_mxfp8(const u32x4* __restrict__ src, int u, int lane,
+                                               bool active, u32x4& q, uint32_t& word) {
+  u32x4 a, b;
+  load_lane16(src, u, active, a, b);
+  quantize_mxfp8(a, b, lane, q, word);
 }
 
 // Payload of one (token t, column slice) work item for each dtype; `rows`
@@ -397,13 +414,18 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_fp8_kernel(
     const int u = slice * 64 + lane;
     // units is a multiple of 8, so each 8-lane group is wholly active or not.
     const bool active = u < units;
+    // x first, then the first batch of row indices: both in flight before
+    // either is waited on.
+    u32x4 a, b;
+    load_lane16(x + static_cast<size_t>(t) * (hidden >> 3), u, active, a, b);
+    int p[kSlotBatch];
+    src_rows.rows_of(t, 0, p);
     u32x4 q;
     float scale;
-    quantize_fp8(x + static_cast<size_t>(t) * (hidden >> 3), u, active, q, scale);
+    quantize_fp8(a, b, q, scale);
     const bool scale_lane = active && (lane & 7) == 0;
     for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
-      int p[kSlotBatch];
-      src_rows.rows_of(t, j0, p);
+      if (j0 > 0) src_rows.rows_of(t, j0, p);
 #pragma unroll
       for (int jj = 0; jj < kSlotBatch; ++jj) {
         if (p[jj] < 0) continue;
@@ -430,13 +452,18 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_mxfp8_kernel(
     const int u = slice * 64 + lane;
     // units is a multiple of 8, so each 8-lane group is wholly active or not.
     const bool active = u < units;
+    // x first, then the first batch of row indices: both in flight before
+    // either is waited on.
+    u32x4 a, b;
+    load_lane16(x + static_cast<size_t>(t) * (hidden >> 3), u, active, a, b);
+    int p[kSlotBatch];
+    src_rows.rows_of(t, 0, p);
     u32x4 q;
     uint32_t word;
-    quantize_mxfp8(x + static_cast<size_t>(t) * (hidden >> 3), u, lane, active, q, word);
+    quantize_mxfp8(a, b, lane, q, word);
     const bool scale_lane = active && (lane & 7) == 0;
     for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
-      int p[kSlotBatch];
-      src_rows.rows_of(t, j0, p);
+      if (j0 > 0) src_rows.rows_of(t, j0, p);
 #pragma unroll
       for (int jj = 0; jj < kSlotBatch; ++jj) {
         if (p[jj] < 0) continue;
