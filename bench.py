@@ -397,6 +397,37 @@ def main():
                                        "frac_of_peak": round(mx / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         for b in sets:
             del b["mx_scales"]
+        # Context, same kernel and method: the bf16 dispatch with its
+        # destination rows in token order. When every slot of token t goes to
+        # expert t*k / (T*k/E) (repeated ids are independent slots), the layout
+        # puts slot (t, j) at row t*k + j: the same bytes as the workload's
+        # routing, with the row writes sequential instead of spread over the E
+        # expert regions at once. Not a figure of the workload.
+        if S % E == 0 and (S // E) % k == 0:
+            rows_per_expert = S // E
+            seq_idx = (torch.arange(T, device=dev, dtype=torch.int32) * k // rows_per_expert)
+            seq_idx = seq_idx.view(T, 1).expand(T, k).contiguous()
+            h.layout(seq_idx)
+            in_order = bool(torch.equal(h.view()["pos"].flatten(),
+                                        torch.arange(S, device=dev, dtype=torch.int32)))
+            evs = [(HipTimer(), HipTimer()) for _ in range(args.sustained_iters)]
+            queue_ahead()
+            for i in range(3 + args.sustained_iters):
+                b = sets[i % len(sets)]
+                if i >= 3:
+                    evs[i - 3][0].record(stream)
+                h.dispatch(b["x"], out=b["d_out"])
+                if i >= 3:
+                    evs[i - 3][1].record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(e) * 1e3 for a, e in evs]))
+            nb = nbytes["dispatch_bf16"]
+            sustained["dispatch_bf16_rows_in_order"] = {
+                "us_median": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "positions_in_order": in_order,
+                "routing": "every slot of token t on expert t*k/(T*k/E), not the workload's"}
+            h.layout(sets[0]["idx"])
 
     # Rank-deduplicated exchange (one row per (token, rank)), sustained method.
     exchange = {}
