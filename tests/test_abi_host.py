@@ -244,3 +244,35 @@ def test_header_compiles_as_c_and_links(tmp_path):
     spec.loader.exec_module(mod)
     out = mod.build(str(tmp_path / "abi_roundtrip"))
     assert os.path.exists(out)
+
+
+def test_binding_records_and_drops_handle_configurations():
+    """The binding keeps each handle's configuration (for its shape checks)
+    from creation to destruction. The library never touches the workspace on
+    the host, so a fake aligned device address serves here."""
+    import combine_moe_dispatch_02_amd as m
+    nbytes = m.moe_workspace_bytes(128, 256, 2, 8, 2)
+    h = m.moe_handle_create(128, 256, 2, 8, 2, 1 << 20, nbytes)
+    try:
+        c = m._CONFIGS[h]
+        assert (c.max_tokens, c.hidden, c.topk, c.num_experts, c.num_ranks) == (128, 256, 2, 8, 2)
+    finally:
+        m.moe_handle_destroy(h)
+    assert h not in m._CONFIGS
+
+
+def test_binding_shape_check():
+    """Width and row-count rules of the binding's shape check (CPU tensors:
+    the check itself looks only at shapes)."""
+    import torch
+    from combine_moe_dispatch_02_amd import _matrix
+    t = torch.empty((6, 4))
+    _matrix(t, "t", 4)
+    _matrix(t, "t", 4, 6)
+    _matrix(None, "t", 4, 100)                      # absent optional tensor
+    with pytest.raises(ValueError, match=r"\[rows, 5\]"):
+        _matrix(t, "t", 5)
+    with pytest.raises(ValueError, match="has 6 rows"):
+        _matrix(t, "t", 4, 7)
+    with pytest.raises(ValueError, match="matrix"):
+        _matrix(torch.empty(24), "t", 4)
