@@ -79,6 +79,38 @@ def edge_ids(T, k, E, pattern, seed=0):
     return ids
 
 
+def test_combine_subnormal_values():
+    """bf16 subnormal rows and products in fp32's subnormal range: combine must
+    keep them (no flush to zero), to the oracle's gate; and an identity round
+    trip whose every term w * x is an exact fp32 subnormal returns x bit for
+    bit (k copies of x / k sum exactly)."""
+    rng = np.random.default_rng(77)
+    T, H, k, E, R = 300, 512, 8, 64, 8
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    S = T * k
+    # y: bf16 subnormals (exponent field 0) and small normals just above them
+    mant = rng.integers(1, 128, size=(S, H)).astype(np.uint16)
+    sign = (rng.random((S, H)) < 0.5).astype(np.uint16) << 15
+    expo = np.where(rng.random((S, H)) < 0.7, 0, rng.integers(1, 4, size=(S, H))).astype(np.uint16)
+    y = sign | (expo << 7) | mant
+    w = rng.uniform(0.01, 1.0, size=(T, k)).astype(np.float32)
+    w[:, 0] = np.float32(2.0 ** -20)   # products far below the smallest bf16 subnormal
+    h = Handle(T, H, k, E, R)
+    h.layout(dev_i32(idx))
+    ref = oracle.layout(idx, E, R)
+    got = host_bits(h.combine(dev_bf16(y), dev_f32(w)))
+    want, mag = oracle.combine(y, w, ref["pos"], return_magnitude=True)
+    _, exact = assert_combine_close(got, want, mag, k)
+    assert exact > 0.9, exact
+    assert np.any(((got & 0x7F80) == 0) & ((got & 0x7FFF) != 0))   # subnormal results survive
+    # identity round trip of subnormal x with weights 1/k: every term exact
+    xs = (sign[:T] | mant[:T]).astype(np.uint16)           # bf16 subnormals (mantissa >= 1)
+    rows = h.dispatch(dev_bf16(xs))
+    back = host_bits(h.combine(rows, dev_f32(np.full((T, k), 1.0 / k, np.float32))))
+    torch.cuda.synchronize()
+    assert np.array_equal(back, xs)
+
+
 @pytest.mark.parametrize("case", EDGE, ids=lambda c: c[0])
 def test_edge_cases_all_ops(case):
     name, T, k, E, R, pattern = case
