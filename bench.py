@@ -5,6 +5,12 @@ layout (histogram + scan + placement), bf16 dispatch, FP8 dispatch, and
 combine of the bf16-dispatched rows (identity experts), on the
 DeepSeek-V3-like shape T=4096, H=7168, E=256 in 8 virtual ranks, top-8.
 
+Every op reads its inputs from HBM: the inputs rotate over enough copies
+(at least COLD_FOOTPRINT bytes of each, 8x the 256 MB last-level cache) that
+none is still cached when it is read again, and the FP8 dispatch reads its
+own copies of x, so it does not find the rows the bf16 dispatch just read.
+Outputs rotate over at least three sets.
+
 GB/s counts algorithmic bytes (each input read once, each output written
 once, index arrays included):
   layout         12*S                      (S = T*k slots: ids in, pos and src_idx out)
@@ -24,6 +30,8 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+LLC_BYTES = 256 << 20    # MI355X last-level (Infinity) cache
+COLD_FOOTPRINT = 2 << 30 # bytes each rotating input spans: 8x the last-level cache
 METRIC = "dispatch & combine HBM GB/s + % of peak, H=7168 T=4096 E=256 top-8"
 WORKLOAD = "deepseekv3"
 
@@ -124,8 +132,8 @@ def queue_ahead():
         _QUEUE_AHEAD_BUF.fill_(i)
 
 
-KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_slots_kernel<TableRows>",
-                "dispatch_fp8": "dispatch_fp8_kernel<TableRows>", "combine": "combine_kernel<true>"}
+KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_slots_kernel",
+                "dispatch_fp8": "dispatch_fp8_kernel", "combine": "combine_kernel<true>"}
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "traffic_deepseekv3.json")
 
@@ -147,39 +155,67 @@ def measured_traffic(op: str):
         return None
 
 
-def cpu_baseline(wl, sample_tokens: int, max_passes: int = 4):
-    """Time the oracle, as committed, on a sample of the same workload."""
+def cpu_baseline(wl, sample_tokens: int, reps: int = 3):
+    """Time the oracle, as committed, on a sample of the same workload.
+
+    The calling thread is pinned to one host CPU and any BLAS/OpenMP pool is
+    limited to one thread for the whole measurement, so "cores" is enforced,
+    not assumed. Each op runs `reps` times; the per-op median is reported and
+    the rate is the sample's algorithmic bytes over the sum of the medians.
+    """
     import oracle
     s = wl.shape
     T, H, k = sample_tokens, s.hidden, s.topk
     x = wl.x_bits[:T]
     idx, w = oracle.route(wl.logits[:T], k, s.weights)   # the routing is not timed
-    # Whole passes of the step over the sample until about 10 s of CPU work.
-    secs = {"layout": 0.0, "dispatch_bf16": 0.0, "dispatch_fp8": 0.0, "combine": 0.0}
-    passes = 0
-    while passes < max_passes and (passes == 0 or sum(secs.values()) < 10.0):
-        t0 = time.perf_counter()
-        lay = oracle.layout(idx, s.experts, s.ranks)
-        t1 = time.perf_counter()
-        y = oracle.dispatch_bf16(x, lay["pos"])
-        t2 = time.perf_counter()
-        oracle.dispatch_fp8(x, lay["pos"])
-        t3 = time.perf_counter()
-        oracle.combine(y, w, lay["pos"])
-        t4 = time.perf_counter()
-        for key, dt in zip(secs, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
-            secs[key] += dt
-        passes += 1
-    total = sum(op_bytes(T, H, k).values()) * passes
-    elapsed = sum(secs.values())
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:   # pragma: no cover - the pin below still holds the thread to one CPU
+        threadpool_limits = None
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    secs = {"layout": [], "dispatch_bf16": [], "dispatch_fp8": [], "combine": []}
+    os.sched_setaffinity(0, {core})
+    try:
+        limits = threadpool_limits(limits=1) if threadpool_limits is not None else None
+        try:
+            cores = len(os.sched_getaffinity(0))
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                lay = oracle.layout(idx, s.experts, s.ranks)
+                t1 = time.perf_counter()
+                y = oracle.dispatch_bf16(x, lay["pos"])
+                t2 = time.perf_counter()
+                oracle.dispatch_fp8(x, lay["pos"])
+                t3 = time.perf_counter()
+                oracle.combine(y, w, lay["pos"])
+                t4 = time.perf_counter()
+                for key, dt in zip(secs, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
+                    secs[key].append(dt)
+        finally:
+            if limits is not None:
+                limits.restore_original_limits()
+    finally:
+        os.sched_setaffinity(0, allowed)
+    med = {key: float(np.median(v)) for key, v in secs.items()}
+    nbytes = op_bytes(T, H, k)
+    total = sum(nbytes.values())
+    elapsed = sum(med.values())
     return {
-        "value": round(total / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"{T} of {s.tokens} tokens of the {s.name} workload, {passes} pass(es) of layout, "
-                  f"bf16 dispatch, FP8 dispatch and combine (numpy, single thread); "
-                  f"{elapsed:.2f} s for {total} algorithmic bytes",
-        "seconds": {key: round(v, 3) for key, v in secs.items()},
+        "value": round(total / elapsed / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": f"{T} of {s.tokens} tokens of the {s.name} workload: layout, bf16 dispatch, FP8 "
+                  f"dispatch and combine (numpy), each run {reps} times on one pinned host CPU "
+                  f"(1 of {len(allowed)} available), per-op median; {elapsed:.2f} s for {total} "
+                  "algorithmic bytes",
+        "seconds_median": {key: round(v, 4) for key, v in med.items()},
+        "GBps_per_op": {key: round(nbytes[key] / med[key] / 1e9, 4) for key in med},
         "host_cpus": os.cpu_count(),
     }
+
+
+def copies_for(nbytes: int, minimum: int = 3) -> int:
+    """How many copies of an nbytes buffer span COLD_FOOTPRINT (at least `minimum`)."""
+    return max(minimum, -(-COLD_FOOTPRINT // max(1, nbytes)))
 
 
 def main():
@@ -188,23 +224,22 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sustained-iters", type=int, default=30,
-                    help="per-op timings, each op back to back over the rotating buffer sets")
+                    help="per-op timings, each op back to back over the rotating buffers")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--workgroup-sweep", type=int, default=1,
                     help="1: also report GB/s against a cap on the payload kernels' workgroups")
-    ap.add_argument("--buffer-sets", type=int, default=3,
-                    help="input/output buffer sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--instrument-every", type=int, default=5,
                     help="record per-op HIP events in every N-th timed step (1: every step)")
     ap.add_argument("--skip", default="",
                     help="comma list of report sections to leave out: rank, decode (router and "
-                         "decode-time path), sweep, others (the other full-size workloads)")
+                         "decode-time path), sweep, others (the other full-size workloads), "
+                         "context (warm-x, evicted-x, in-order and copy/fill figures)")
     args = ap.parse_args()
 
     skip = {x for x in args.skip.split(",") if x}
-    if not skip <= {"rank", "decode", "sweep", "others"}:
-        ap.error(f"--skip takes rank, decode, sweep, others; got {args.skip}")
+    if not skip <= {"rank", "decode", "sweep", "others", "context"}:
+        ap.error(f"--skip takes rank, decode, sweep, others, context; got {args.skip}")
     if args.steps < 1:
         ap.error("--steps must be at least 1")
     if "sweep" in skip:
@@ -229,40 +264,49 @@ def main():
     topk_idx, topk_w = h.route(logits, s.weights)
     torch.cuda.synchronize()
 
-    # Consecutive steps use different buffer sets (inputs and outputs, about
-    # 0.84 GB each), so no step finds the previous step's data in the 256 MB
-    # last-level cache: every step's bytes come from and go to HBM.
     S = T * k
-    sets = []
-    for _ in range(args.buffer_sets):
-        sets.append({
-            "x": torch.from_numpy(wl.x_bits.view(np.int16)).view(torch.bfloat16).to(dev),
-            "idx": topk_idx.clone(),
-            "w": topk_w.clone(),
-            "d_out": torch.empty((S, H), dtype=torch.bfloat16, device=dev),
-            "q_out": torch.empty((S, H), dtype=torch.uint8, device=dev),
-            "q_scales": torch.empty((S, H // 128), dtype=torch.float32, device=dev),
-            "c_out": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
-        })
-    ops = ("layout", "dispatch_bf16", "dispatch_fp8", "combine")
-    cur = {"i": 0}
+    x_dev = torch.from_numpy(wl.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    x_bytes = 2 * T * H
+    # Inputs rotate over copies spanning COLD_FOOTPRINT each; the FP8 dispatch
+    # has copies of its own. Outputs rotate over three sets (combine's input,
+    # the bf16 dispatch's output, over as many as span COLD_FOOTPRINT).
+    n_x = copies_for(x_bytes)
+    n_d = copies_for(2 * S * H)
+    bufs = {
+        "xb": [x_dev.clone() for _ in range(n_x)],
+        "xq": [x_dev.clone() for _ in range(n_x)],
+        "idx": [topk_idx.clone() for _ in range(3)],
+        "w": [topk_w.clone() for _ in range(3)],
+        "d_out": [torch.empty((S, H), dtype=torch.bfloat16, device=dev) for _ in range(n_d)],
+        "q_out": [torch.empty((S, H), dtype=torch.uint8, device=dev) for _ in range(3)],
+        "q_scales": [torch.empty((S, H // 128), dtype=torch.float32, device=dev) for _ in range(3)],
+        "c_out": [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(3)],
+    }
 
-    def run_op(name):
-        b = sets[cur["i"]]
+    def B(key, i):
+        lst = bufs[key]
+        return lst[i % len(lst)]
+
+    ops = ("layout", "dispatch_bf16", "dispatch_fp8", "combine")
+
+    def run_op(name, i):
         if name == "layout":
-            h.layout(b["idx"])
+            h.layout(B("idx", i))
         elif name == "dispatch_bf16":
-            h.dispatch(b["x"], out=b["d_out"])
+            h.dispatch(B("xb", i), out=B("d_out", i))
         elif name == "dispatch_fp8":
-            h.dispatch(b["x"], fp8=True, out=b["q_out"], scales=b["q_scales"])
+            h.dispatch(B("xq", i), fp8=True, out=B("q_out", i), scales=B("q_scales", i))
         else:
-            h.combine(b["d_out"], b["w"], out=b["c_out"])
+            h.combine(B("d_out", i), B("w", i), out=B("c_out", i))
 
     stream = torch.cuda.current_stream(dev)
+    # Every expert-row set holds dispatched rows before anything reads it.
+    h.layout(bufs["idx"][0])
+    for i in range(n_d):
+        h.dispatch(B("xb", i), out=B("d_out", i))
     for i in range(args.warmup):
-        cur["i"] = i % len(sets)
         for name in ops:
-            run_op(name)
+            run_op(name, i)
     torch.cuda.synchronize()
 
     # Timed region: exactly K steps. Every `instrument_every`-th step (steps
@@ -275,20 +319,19 @@ def main():
     # time per step carries as little timing overhead as possible.
     every = max(1, args.instrument_every)
     instrumented = [i for i in range(args.steps) if i % every == every - 1] or [args.steps - 1]
-    ev = {i: [HipTimer() for _ in range(len(ops) + 1)]
-          for i in instrumented}
+    ev = {i: [HipTimer() for _ in range(len(ops) + 1)] for i in instrumented}
+    base = args.warmup
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        cur["i"] = i % len(sets)
         marks = ev.get(i)
         if marks is None:
             for name in ops:
-                run_op(name)
+                run_op(name, base + i)
             continue
         marks[0].record(stream)
         for j, name in enumerate(ops):
-            run_op(name)
+            run_op(name, base + i)
             marks[j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -304,100 +347,94 @@ def main():
                         "GBps": round(nbytes[name] / (us.mean() * 1e-6) / 1e9, 1),
                         "frac_of_peak": round(nbytes[name] / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    # Sustained per-op timings: each op alone, back to back over the rotating
-    # buffer sets. Every call finds the previous call's dirty lines in the
-    # last-level cache and leaves as many behind, so each call pays for its
-    # own writes reaching HBM (timing one call after a cache flush would not).
+    def sustained_us(fn, iters, first=0, stats=False):
+        """Median us of fn(i), i = first, first+1, ..., over back-to-back calls
+        (3 untimed first), with the GPU queued ahead of the loop."""
+        evs = [(HipTimer(), HipTimer()) for _ in range(iters)]
+        queue_ahead()
+        for i in range(3 + iters):
+            if i >= 3:
+                evs[i - 3][0].record(stream)
+            fn(first + i)
+            if i >= 3:
+                evs[i - 3][1].record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        if not stats:
+            return round(float(np.median(us)), 2)
+        return {"us_median": round(float(np.median(us)), 2),
+                "us_p10": round(float(np.percentile(us, 10)), 2),
+                "us_p90": round(float(np.percentile(us, 90)), 2)}
+
+    def rate(nb, us):
+        return {"GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    # Sustained per-op timings: each op alone, back to back over the same
+    # rotating buffers (inputs from HBM). Every call finds the previous
+    # call's dirty lines in the last-level cache and leaves as many behind, so
+    # each call pays for its own writes reaching HBM.
     sustained = {}
+    context = {}
     if args.sustained_iters > 0:
         for name in ops:
-            evs = [(HipTimer(), HipTimer())
-                   for _ in range(args.sustained_iters)]
-            queue_ahead()
-            for i in range(3 + args.sustained_iters):
-                cur["i"] = i % len(sets)
-                if i >= 3:
-                    evs[i - 3][0].record(stream)
-                run_op(name)
-                if i >= 3:
-                    evs[i - 3][1].record(stream)
-            torch.cuda.synchronize()
-            us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
-            sustained[name] = {"us_median": round(float(np.median(us)), 2),
-                               "us_p10": round(float(np.percentile(us, 10)), 2),
-                               "us_p90": round(float(np.percentile(us, 90)), 2),
-                               "GBps": round(nbytes[name] / (np.median(us) * 1e-6) / 1e9, 1),
-                               "frac_of_peak": round(nbytes[name] / (np.median(us) * 1e-6) / 1e9
-                                                     / HBM_PEAK_GBS, 4)}
-        # Context, same method: torch's device-to-device copy of the bf16
-        # dispatch's byte count (half read, half written) and a plain write
-        # (fill) of the bf16 dispatch's output size.
-        half = nbytes["dispatch_bf16"] // 2
-        wbytes = S * H * 2
-        bufs = [torch.empty(max(wbytes, 2 * half), dtype=torch.uint8, device=dev) for _ in range(3)]
-        for label, moved, fn in (("copy_same_bytes", 2 * half, lambda b: b[half:2 * half].copy_(b[:half])),
-                                 ("write_same_bytes", wbytes, lambda b: b[:wbytes].fill_(7))):
-            evs = [(HipTimer(), HipTimer())
-                   for _ in range(args.sustained_iters)]
-            queue_ahead()
-            for i in range(3 + args.sustained_iters):
-                if i >= 3:
-                    evs[i - 3][0].record(stream)
-                fn(bufs[i % 3])
-                if i >= 3:
-                    evs[i - 3][1].record(stream)
-            torch.cuda.synchronize()
-            us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
-            sustained[label] = {"bytes": moved, "us_median": round(float(np.median(us)), 2),
-                                "GBps": round(moved / (np.median(us) * 1e-6) / 1e9, 1)}
-        del bufs
-        # Context: the two dispatches with x evicted from the last-level cache.
-        # Across the rotating sets x (2*T*H bytes per set) stays cache-resident:
-        # the dispatches' non-temporal row stores and combine's non-temporal
-        # loads do not displace it. Here every timed call follows a 1 GiB read
-        # sweep (a reduction; no dirty lines), outside its events.
+            st = sustained_us(lambda i, n=name: run_op(n, i), args.sustained_iters, stats=True)
+            st.update(rate(nbytes[name], st["us_median"]))
+            sustained[name] = st
+        # MXFP8 dispatch (32-channel blocks, E8M0 scales), same method.
+        mx_scales = [torch.empty((S, H // 32), dtype=torch.uint8, device=dev) for _ in range(3)]
+        mx = mxfp8_bytes(T, H, k)
+        us = sustained_us(lambda i: h.dispatch(B("xq", i), mxfp8=True, out=B("q_out", i),
+                                               scales=mx_scales[i % 3]), args.sustained_iters)
+        sustained["dispatch_mxfp8"] = {"bytes": mx, "us_median": us, **rate(mx, us)}
+        del mx_scales
+
+    if args.sustained_iters > 0 and "context" not in skip:
+        # Context 1: the two dispatches reading one copy of x over and over, so
+        # that x (2*T*H bytes) stays in the last-level cache -- as when the op
+        # before dispatch has just written it. Not the headline.
+        warm = {}
+        for name, fn in (("dispatch_bf16", lambda i: h.dispatch(bufs["xb"][0], out=B("d_out", i))),
+                         ("dispatch_fp8", lambda i: h.dispatch(bufs["xb"][0], fp8=True,
+                                                               out=B("q_out", i),
+                                                               scales=B("q_scales", i)))):
+            us = sustained_us(fn, args.sustained_iters)
+            warm[name] = {"us_median": us, **rate(nbytes[name], us)}
+        context["x_cache_resident"] = warm
+        # Context 2: a cross-check of the cold-input method -- every timed call
+        # follows a 1 GiB read sweep (a reduction; no dirty lines), outside its
+        # events.
         sweep_src = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
         sink = torch.zeros((), dtype=torch.float32, device=dev)
         evicted = {}
         for name in ("dispatch_bf16", "dispatch_fp8"):
             evs = [(HipTimer(), HipTimer()) for _ in range(args.sustained_iters)]
             for i in range(3 + args.sustained_iters):
-                cur["i"] = i % len(sets)
                 sink.copy_(sweep_src.amax())
                 if i >= 3:
                     evs[i - 3][0].record(stream)
-                run_op(name)
+                run_op(name, i)
                 if i >= 3:
                     evs[i - 3][1].record(stream)
             torch.cuda.synchronize()
             us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
-            evicted[name] = {"us_median": round(us, 2),
-                             "GBps": round(nbytes[name] / (us * 1e-6) / 1e9, 1)}
-        sustained["x_evicted"] = evicted
+            evicted[name] = {"us_median": round(us, 2), **rate(nbytes[name], us)}
+        context["x_evicted_by_sweep"] = evicted
         del sweep_src, sink
-        # MXFP8 dispatch (32-channel blocks, E8M0 scales), same method.
-        for b in sets:
-            b["mx_scales"] = torch.empty((S, H // 32), dtype=torch.uint8, device=dev)
-        mx = mxfp8_bytes(T, H, k)
-        evs = [(HipTimer(), HipTimer())
-               for _ in range(args.sustained_iters)]
-        h.layout(sets[0]["idx"])
-        queue_ahead()
-        for i in range(3 + args.sustained_iters):
-            b = sets[i % len(sets)]
-            if i >= 3:
-                evs[i - 3][0].record(stream)
-            h.dispatch(b["x"], mxfp8=True, out=b["q_out"], scales=b["mx_scales"])
-            if i >= 3:
-                evs[i - 3][1].record(stream)
-        torch.cuda.synchronize()
-        us = float(np.median([a.elapsed_time(e) * 1e3 for a, e in evs]))
-        sustained["dispatch_mxfp8"] = {"bytes": mx, "us_median": round(us, 2),
-                                       "GBps": round(mx / (us * 1e-6) / 1e9, 1),
-                                       "frac_of_peak": round(mx / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        for b in sets:
-            del b["mx_scales"]
-        # Context, same kernel and method: the bf16 dispatch with its
+        # Context 3: torch's device-to-device copy of the bf16 dispatch's byte
+        # count (half read, half written) and a plain write (fill) of the bf16
+        # dispatch's output size, same method.
+        half = nbytes["dispatch_bf16"] // 2
+        wbytes = S * H * 2
+        cbufs = [torch.empty(max(wbytes, 2 * half), dtype=torch.uint8, device=dev) for _ in range(3)]
+        for label, moved, fn in (("copy_same_bytes", 2 * half,
+                                  lambda b: b[half:2 * half].copy_(b[:half])),
+                                 ("write_same_bytes", wbytes, lambda b: b[:wbytes].fill_(7))):
+            us = sustained_us(lambda i, f=fn: f(cbufs[i % 3]), args.sustained_iters)
+            context[label] = {"bytes": moved, "us_median": us,
+                              "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
+        del cbufs
+        # Context 4, same kernel and method: the bf16 dispatch with its
         # destination rows in token order. When every slot of token t goes to
         # expert t*k / (T*k/E) (repeated ids are independent slots), the layout
         # puts slot (t, j) at row t*k + j: the same bytes as the workload's
@@ -410,116 +447,74 @@ def main():
             h.layout(seq_idx)
             in_order = bool(torch.equal(h.view()["pos"].flatten(),
                                         torch.arange(S, device=dev, dtype=torch.int32)))
-            evs = [(HipTimer(), HipTimer()) for _ in range(args.sustained_iters)]
-            queue_ahead()
-            for i in range(3 + args.sustained_iters):
-                b = sets[i % len(sets)]
-                if i >= 3:
-                    evs[i - 3][0].record(stream)
-                h.dispatch(b["x"], out=b["d_out"])
-                if i >= 3:
-                    evs[i - 3][1].record(stream)
-            torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_time(e) * 1e3 for a, e in evs]))
-            nb = nbytes["dispatch_bf16"]
-            sustained["dispatch_bf16_rows_in_order"] = {
-                "us_median": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
-                "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            us = sustained_us(lambda i: h.dispatch(B("xb", i), out=B("d_out", i)),
+                              args.sustained_iters)
+            context["dispatch_bf16_rows_in_order"] = {
+                "us_median": us, **rate(nbytes["dispatch_bf16"], us),
                 "positions_in_order": in_order,
                 "routing": "every slot of token t on expert t*k/(T*k/E), not the workload's"}
-            h.layout(sets[0]["idx"])
+            h.layout(bufs["idx"][0])
 
     # Rank-deduplicated exchange (one row per (token, rank)), sustained method.
     exchange = {}
     if args.sustained_iters > 0 and "rank" not in skip:
-        h.rank_layout(sets[0]["idx"])
+        h.rank_layout(bufs["idx"][0])
         torch.cuda.synchronize()
         rows = int(h.rank_view()["status"][0].item())
         cap = h.rank_capacity
-        for b in sets:
-            b["r_out"] = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
-            b["r_idx"] = torch.empty((cap, k), dtype=torch.int32, device=dev)
-            b["r_w"] = torch.empty((cap, k), dtype=torch.float32, device=dev)
+        rb = [{"out": torch.empty((cap, H), dtype=torch.bfloat16, device=dev),
+               "idx": torch.empty((cap, k), dtype=torch.int32, device=dev),
+               "w": torch.empty((cap, k), dtype=torch.float32, device=dev)}
+              for _ in range(copies_for(2 * cap * H))]
+        RB = lambda i: rb[i % len(rb)]   # noqa: E731
         xb = {"rank_layout": 4 * S + 4 * S + 4 * T * R + 4 * rows,
               "dispatch_ranks": 2 * T * H + 2 * rows * H + 8 * rows * k + 12 * S,
               "combine_ranks": 2 * rows * H + 2 * T * H + 4 * T * R}
-        calls = {"rank_layout": lambda b: h.rank_layout(b["idx"]),
-                 "dispatch_ranks": lambda b: h.dispatch_ranks(b["x"], b["idx"], b["w"], out=b["r_out"],
-                                                              recv_idx=b["r_idx"], recv_w=b["r_w"]),
-                 "combine_ranks": lambda b: h.combine_ranks(b["r_out"], out=b["c_out"])}
+        calls = {"rank_layout": lambda i: h.rank_layout(B("idx", i)),
+                 "dispatch_ranks": lambda i: h.dispatch_ranks(B("xb", i), B("idx", i), B("w", i),
+                                                              out=RB(i)["out"],
+                                                              recv_idx=RB(i)["idx"],
+                                                              recv_w=RB(i)["w"]),
+                 "combine_ranks": lambda i: h.combine_ranks(RB(i)["out"], out=B("c_out", i))}
+        for i in range(len(rb)):
+            calls["dispatch_ranks"](i)
         for name, fn in calls.items():
-            evs = [(HipTimer(), HipTimer())
-                   for _ in range(args.sustained_iters)]
-            queue_ahead()
-            for i in range(3 + args.sustained_iters):
-                if i >= 3:
-                    evs[i - 3][0].record(stream)
-                fn(sets[i % len(sets)])
-                if i >= 3:
-                    evs[i - 3][1].record(stream)
-            torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_time(e) * 1e3 for a, e in evs]))
-            exchange[name] = {"bytes": xb[name], "us_median": round(us, 2),
+            us = sustained_us(fn, args.sustained_iters)
+            exchange[name] = {"bytes": xb[name], "us_median": us,
                               "GBps": round(xb[name] / (us * 1e-6) / 1e9, 1)}
         exchange["rows"] = rows
         exchange["rows_without_dedup"] = S
-        for b in sets:
-            del b["r_out"], b["r_idx"], b["r_w"]
+        del rb
 
     # Bandwidth against the number of workgroups (4 wavefronts each) the payload
     # kernels may use (moe_set_max_workgroups), sustained method, 256 CUs.
     sweep = {}
     if args.workgroup_sweep:
-        for cap in (16, 32, 64, 128, 256, 512, 1024, 0):
-            h.set_max_workgroups(cap)
+        for capw in (16, 32, 64, 128, 256, 512, 1024, 0):
+            h.set_max_workgroups(capw)
             row = {}
             for name in ("dispatch_bf16", "dispatch_fp8", "combine"):
-                evs = [(HipTimer(), HipTimer())
-                       for _ in range(5)]
-                queue_ahead()
-                for i in range(7):
-                    cur["i"] = i % len(sets)
-                    if i >= 2:
-                        evs[i - 2][0].record(stream)
-                    run_op(name)
-                    if i >= 2:
-                        evs[i - 2][1].record(stream)
-                torch.cuda.synchronize()
-                us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+                us = sustained_us(lambda i, n=name: run_op(n, i), 5)
                 row[name] = round(nbytes[name] / (us * 1e-6) / 1e9, 1)
-            sweep["uncapped" if cap == 0 else str(cap)] = row
+            sweep["uncapped" if capw == 0 else str(capw)] = row
         h.set_max_workgroups(0)
-
-    def sustained_us(fn, iters):
-        """Median µs of fn(i) over back-to-back calls (3 untimed first)."""
-        evs = [(HipTimer(), HipTimer())
-               for _ in range(iters)]
-        queue_ahead()
-        for i in range(3 + iters):
-            if i >= 3:
-                evs[i - 3][0].record(stream)
-            fn(i)
-            if i >= 3:
-                evs[i - 3][1].record(stream)
-        torch.cuda.synchronize()
-        return round(float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs])), 2)
 
     # Router at the prefill shape, and the decode-time path at 128 tokens
     # (fixed per-expert capacity 128: no slot can be dropped).
     router, decode = {}, {}
     if args.sustained_iters > 0 and "decode" not in skip:
         rbytes = 4 * T * E + 8 * T * k
-        lg = [logits.clone() for _ in range(len(sets))]
-        us = sustained_us(lambda i: h.route(lg[i % len(lg)], s.weights, topk_idx=sets[0]["idx"],
-                                            topk_w=sets[0]["w"]), args.sustained_iters)
+        lg = [logits.clone() for _ in range(copies_for(4 * T * E))]
+        us = sustained_us(lambda i: h.route(lg[i % len(lg)], s.weights, topk_idx=B("idx", i),
+                                            topk_w=B("w", i)), args.sustained_iters)
         router = {"tokens": T, "experts": E, "topk": k, "score": s.weights, "bytes": rbytes,
                   "us_median": us, "GBps": round(rbytes / (us * 1e-6) / 1e9, 1)}
         Td, C = 128, 128
         hd = Handle(Td, H, k, E, R, device=dev)
         dsets = []
-        for b in sets:
+        for i in range(3):
             di, dw = hd.route(logits[:Td].contiguous(), s.weights)
-            dsets.append({"idx": di, "w": dw, "x": b["x"][:Td].contiguous(),
+            dsets.append({"idx": di, "w": dw, "x": B("xb", i)[:Td].contiguous(),
                           "lg": logits[:Td].clone(),
                           "out": torch.empty((E * C, H), dtype=torch.bfloat16, device=dev),
                           "q": torch.empty((E * C, H), dtype=torch.uint8, device=dev),
@@ -549,7 +544,9 @@ def main():
         decode["payload_bytes_bf16"] = 2 * Td * H + 2 * Td * k * H
 
         # The whole decode step (router -> decode-time dispatch -> combine of the
-        # dispatched rows), eagerly and replayed as one captured HIP graph.
+        # dispatched rows): eagerly, replayed as one captured HIP graph per
+        # step, and as one graph holding ten steps (per-step figure), which
+        # separates the graph launch's own cost from the kernels'.
         g0 = dsets[0]
 
         def decode_step():
@@ -561,10 +558,16 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             decode_step()
+        graph10 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph10):
+            for _ in range(10):
+                decode_step()
         torch.cuda.synchronize()
         decode["step_eager_us"] = sustained_us(lambda i: decode_step(), args.sustained_iters)
         decode["step_graph_us"] = sustained_us(lambda i: graph.replay(), args.sustained_iters)
-        del graph, dsets, hd
+        decode["step_in_10_step_graph_us"] = round(
+            sustained_us(lambda i: graph10.replay(), max(5, args.sustained_iters // 3)) / 10, 2)
+        del graph, graph10, dsets, hd
 
         # Decode-time dispatch (fixed capacity = T, nothing dropped) and the
         # one-launch packed layout + dispatch against the two calls, over batch
@@ -573,7 +576,7 @@ def main():
         for Tn in (32, 128, 512, 1024):
             hn = Handle(Tn, H, k, E, R, device=dev)
             ni, _ = hn.route(logits[:Tn].contiguous(), s.weights)
-            nx = sets[0]["x"][:Tn].contiguous()
+            nx = bufs["xb"][0][:Tn].contiguous()
             n_ll = torch.empty((E * Tn, H), dtype=torch.bfloat16, device=dev)
             n_std = torch.empty((Tn * k, H), dtype=torch.bfloat16, device=dev)
 
@@ -590,42 +593,56 @@ def main():
         decode["by_tokens"] = scaling
 
     # The other full-size workloads (not the headline): sustained per-op
-    # rates, 3 rotating buffer sets each, routing by the router kernel.
+    # rates with inputs from HBM (the same rotation rule), routing by the
+    # router kernel; plus the two dispatches reading one cached copy of x.
     others = {}
     if args.sustained_iters > 0 and "others" not in skip:
         for name in ("deepseek16b", "qwen3_skewed"):
             wo = make_workload(name)
             so = wo.shape
             To, Ho, ko = so.tokens, so.hidden, so.topk
+            So = To * ko
             ho = Handle(To, Ho, ko, so.experts, so.ranks, device=dev)
             oi, ow = ho.route(torch.from_numpy(wo.logits).to(dev), so.weights)
             xo = torch.from_numpy(wo.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-            So = To * ko
-            osets = [{"idx": oi.clone(), "w": ow.clone(), "x": xo.clone(),
-                      "d": torch.empty((So, Ho), dtype=torch.bfloat16, device=dev),
-                      "q": torch.empty((So, Ho), dtype=torch.uint8, device=dev),
-                      "qs": torch.empty((So, Ho // 128), dtype=torch.float32, device=dev),
-                      "c": torch.empty((To, Ho), dtype=torch.bfloat16, device=dev)} for _ in range(3)]
+            ob_ = {"x": [xo.clone() for _ in range(copies_for(2 * To * Ho))],
+                   "idx": [oi.clone() for _ in range(3)], "w": [ow.clone() for _ in range(3)],
+                   "d": [torch.empty((So, Ho), dtype=torch.bfloat16, device=dev)
+                         for _ in range(copies_for(2 * So * Ho))],
+                   "q": [torch.empty((So, Ho), dtype=torch.uint8, device=dev) for _ in range(3)],
+                   "qs": [torch.empty((So, Ho // 128), dtype=torch.float32, device=dev)
+                          for _ in range(3)],
+                   "c": [torch.empty((To, Ho), dtype=torch.bfloat16, device=dev) for _ in range(3)]}
             del xo
-            O = lambda i: osets[i % 3]   # noqa: E731
-            ob = op_bytes(To, Ho, ko)
-            calls = {"layout": lambda i: ho.layout(O(i)["idx"]),
-                     "dispatch_bf16": lambda i: ho.dispatch(O(i)["x"], out=O(i)["d"]),
-                     "dispatch_fp8": lambda i: ho.dispatch(O(i)["x"], fp8=True, out=O(i)["q"],
-                                                           scales=O(i)["qs"]),
-                     "combine": lambda i: ho.combine(O(i)["d"], O(i)["w"], out=O(i)["c"])}
-            for i in range(3):                    # lay out every set once before timing combine
-                ho.layout(O(i)["idx"])
-            row = {"tokens": To, "hidden": Ho, "experts": so.experts, "topk": ko}
+            O = lambda key, i: ob_[key][i % len(ob_[key])]   # noqa: E731
+            nb = op_bytes(To, Ho, ko)
+            calls = {"layout": lambda i: ho.layout(O("idx", i)),
+                     "dispatch_bf16": lambda i: ho.dispatch(O("x", i), out=O("d", i)),
+                     "dispatch_fp8": lambda i: ho.dispatch(O("x", i), fp8=True, out=O("q", i),
+                                                           scales=O("qs", i)),
+                     "combine": lambda i: ho.combine(O("d", i), O("w", i), out=O("c", i))}
+            ho.layout(ob_["idx"][0])
+            for i in range(len(ob_["d"])):   # every expert-row set holds dispatched rows
+                calls["dispatch_bf16"](i)
+            row = {"tokens": To, "hidden": Ho, "experts": so.experts, "topk": ko,
+                   "x_copies": len(ob_["x"]), "expert_row_sets": len(ob_["d"])}
             for op, fn in calls.items():
                 us = sustained_us(fn, args.sustained_iters)
-                row[op] = {"us_median": us, "GBps": round(ob[op] / (us * 1e-6) / 1e9, 1)}
+                row[op] = {"us_median": us, **rate(nb[op], us)}
+            warm = {}
+            for op, fn in (("dispatch_bf16", lambda i: ho.dispatch(ob_["x"][0], out=O("d", i))),
+                           ("dispatch_fp8", lambda i: ho.dispatch(ob_["x"][0], fp8=True,
+                                                                  out=O("q", i), scales=O("qs", i)))):
+                us = sustained_us(fn, args.sustained_iters)
+                warm[op] = {"us_median": us, **rate(nb[op], us)}
+            row["x_cache_resident"] = warm
             others[name] = row
-            del osets, ho
+            del ob_, ho
         torch.cuda.synchronize()
 
     dominant = max(("dispatch_bf16", "dispatch_fp8", "combine"), key=lambda n: per_op[n]["us_mean"])
     achieved = per_op[dominant]["GBps"]
+    traffic = measured_traffic(dominant)
     result = {
         "metric": METRIC,
         "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -640,16 +657,24 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{WORKLOAD}: T={T} H={H} E={E} in R={R} virtual ranks, top-{k}; "
-                               "layout + bf16 dispatch + FP8 dispatch + bf16 combine",
+                               "layout + bf16 dispatch + FP8 dispatch + bf16 combine, every input "
+                               "read from HBM",
                    "tokens": T, "hidden": H, "experts": E, "virtual_ranks": R, "topk": k,
-                   "buffer_sets": len(sets)},
+                   "x_copies_per_dispatch": n_x, "expert_row_sets": n_d},
         "frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_source": (f"{os.path.relpath(TRAFFIC_FILE, os.path.dirname(os.path.abspath(__file__)))}"
+                                        f" [{KERNEL_OF_OP[dominant]}]: rocprofv3 FETCH_SIZE + "
+                                        "WRITE_SIZE per launch, copy-calibrated, taken from "
+                                        "the same kernel source (hash-checked)")
+                     if traffic is not None else
+                     "none: the kernel's source changed since the counters were taken"},
         "ops": per_op,
         "instrumented_steps": len(instrumented),
         "sustained": sustained,
+        "context": context,
         "workgroup_sweep_GBps": sweep,
         "rank_exchange": exchange,
         "router": router,

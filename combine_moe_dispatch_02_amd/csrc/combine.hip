@@ -1,9 +1,10 @@
 // Combine: gather each token's k expert-output rows back to token order as a
 // router-weighted sum.
 //
-// Per the pages, combine "returns expert outputs to their original positions"
-// ("Inside the Nebius + PyTorch DeepSeek V3 recipe", section "Mixture-of-experts
-// and wide expert parallelism"). Here that is
+// Combine is the second half of an MoE layer's exchange: the expert outputs
+// go back to the positions their tokens came from ("Inside the Nebius +
+// PyTorch DeepSeek V3 recipe", section "Mixture-of-experts and wide expert
+// parallelism"). Here that is
 //   out[t] = bf16_rne( sum_{j = 0..k-1, pos[t,j] >= 0} w[t,j] * y[pos[t,j]] )
 // accumulated in fp32 in the fixed slot order j = 0, 1, ..., k-1 (one fused
 // multiply-add per term, starting from +0), so the result does not depend on
@@ -44,15 +45,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
 
-__device__ __forceinline__ void accumulate(float (&acc)[8], float w, const u32x4& r) {
-  acc[0] = __builtin_fmaf(w, bf16_lo(r.x), acc[0]);
-  acc[1] = __builtin_fmaf(w, bf16_hi(r.x), acc[1]);
-  acc[2] = __builtin_fmaf(w, bf16_lo(r.y), acc[2]);
-  acc[3] = __builtin_fmaf(w, bf16_hi(r.y), acc[3]);
-  acc[4] = __builtin_fmaf(w, bf16_lo(r.z), acc[4]);
-  acc[5] = __builtin_fmaf(w, bf16_hi(r.z), acc[5]);
-  acc[6] = __builtin_fmaf(w, bf16_lo(r.w), acc[6]);
-  acc[7] = __builtin_fmaf(w, bf16_hi(r.w), acc[7]);
+// acc += w * row (one fused multiply-add per channel) when `use`, else acc is
+// left exactly as it is (a select, so that the loads of every slot still
+// issue together; adding a zero product instead would turn an acc of -0 into
+// +0).
+__device__ __forceinline__ void accumulate(float (&acc)[8], bool use, float w, const u32x4& r) {
+  const float f[8] = {bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y),
+                      bf16_lo(r.z), bf16_hi(r.z), bf16_lo(r.w), bf16_hi(r.w)};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = use ? __builtin_fmaf(w, f[i], acc[i]) : acc[i];
 }
 
 // kWeighted = false sums the rows unweighted (weight 1, w unused): the final
@@ -105,14 +106,10 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(
 #pragma unroll
       for (int jj = 0; jj < kSlotBatch; ++jj)
         r[jj] = __builtin_nontemporal_load(&y[static_cast<size_t>(p[jj]) * nvec + vc]);
-      // Unused slots add w * y with both zeroed: fma(0, 0, acc) == acc exactly
-      // (acc is never -0: it starts at +0 and an exact-zero sum rounds to +0).
-      // Selecting instead of branching keeps the loads above in one batch.
+      // Unused slots leave acc untouched; selecting instead of branching keeps
+      // the loads above in one batch.
 #pragma unroll
-      for (int jj = 0; jj < kSlotBatch; ++jj) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        accumulate(acc, use[jj] ? wj[jj] : 0.0f, use[jj] ? r[jj] : z);
-      }
+      for (int jj = 0; jj < kSlotBatch; ++jj) accumulate(acc, use[jj], wj[jj], r[jj]);
     }
     if (active) {
       u32x4 o;
