@@ -234,12 +234,13 @@ def main():
     ap.add_argument("--skip", default="",
                     help="comma list of report sections to leave out: rank, decode (router and "
                          "decode-time path), sweep, others (the other full-size workloads), "
-                         "context (warm-x, evicted-x, in-order and copy/fill figures)")
+                         "context (warm-x, evicted-x, in-order and copy/fill figures), cus "
+                         "(compute-unit-limited streams, with a concurrent GEMM)")
     args = ap.parse_args()
 
     skip = {x for x in args.skip.split(",") if x}
-    if not skip <= {"rank", "decode", "sweep", "others", "context"}:
-        ap.error(f"--skip takes rank, decode, sweep, others, context; got {args.skip}")
+    if not skip <= {"rank", "decode", "sweep", "others", "context", "cus"}:
+        ap.error(f"--skip takes rank, decode, sweep, others, context, cus; got {args.skip}")
     if args.steps < 1:
         ap.error("--steps must be at least 1")
     if "sweep" in skip:
@@ -349,15 +350,17 @@ def main():
 
     def sustained_us(fn, iters, first=0, stats=False):
         """Median us of fn(i), i = first, first+1, ..., over back-to-back calls
-        (3 untimed first), with the GPU queued ahead of the loop."""
+        (3 untimed first) on torch's current stream, with the GPU queued ahead
+        of the loop."""
+        cur = torch.cuda.current_stream(dev)
         evs = [(HipTimer(), HipTimer()) for _ in range(iters)]
         queue_ahead()
         for i in range(3 + iters):
             if i >= 3:
-                evs[i - 3][0].record(stream)
+                evs[i - 3][0].record(cur)
             fn(first + i)
             if i >= 3:
-                evs[i - 3][1].record(stream)
+                evs[i - 3][1].record(cur)
         torch.cuda.synchronize()
         us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
         if not stats:
@@ -498,6 +501,86 @@ def main():
                 row[name] = round(nbytes[name] / (us * 1e-6) / 1e9, 1)
             sweep["uncapped" if capw == 0 else str(capw)] = row
         h.set_max_workgroups(0)
+
+    # Compute-unit-limited streams: each payload op on n compute units (an
+    # equal share of every XCD, moe_stream_create_cu_limited), then the bf16
+    # dispatch and combine on n units concurrently with a bf16 GEMM
+    # (8192 x 8192 x 8192, torch) on a stream limited to the other 256 - n.
+    cu_limited = {}
+    if args.sustained_iters > 0 and "cus" not in skip:
+        from combine_moe_dispatch_02_amd import CuLimitedStream
+        total_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        by_cus = {}
+        for n in (8, 16, 32, 64, 128, total_cus):
+            with CuLimitedStream(n, dev):
+                row = {}
+                for name in ("dispatch_bf16", "dispatch_fp8", "combine"):
+                    us = sustained_us(lambda i, nm=name: run_op(nm, i), 5 if n < 64 else 10)
+                    row[name] = round(nbytes[name] / (us * 1e-6) / 1e9, 1)
+            by_cus[str(n)] = row
+        cu_limited["GBps_by_cus"] = by_cus
+        gm = 8192
+        ga = torch.randn((gm, gm), dtype=torch.bfloat16, device=dev)
+        gb = torch.randn((gm, gm), dtype=torch.bfloat16, device=dev)
+        gc = torch.empty((gm, gm), dtype=torch.bfloat16, device=dev)
+        gflop = 2.0 * gm ** 3
+
+        def gemm(i):
+            torch.mm(ga, gb, out=gc)
+
+        def window(calls, streams, counts):
+            """Run calls[s](i) for i < counts[s] on each stream, interleaved in
+            issue order; returns each stream's elapsed us (HIP events)."""
+            evs = [(HipTimer(), HipTimer()) for _ in streams]
+            for (a, _), st in zip(evs, streams):
+                a.record(st)
+            for i in range(max(counts)):
+                for s, st in enumerate(streams):
+                    if i < counts[s]:
+                        with torch.cuda.stream(st):
+                            calls[s](i)
+            for (_, b), st in zip(evs, streams):
+                b.record(st)
+            torch.cuda.synchronize()
+            return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+        # the GEMM alone on every compute unit, for reference
+        for i in range(3):
+            gemm(i)
+        t_all = window([gemm], [stream], [20])[0] / 20
+        cu_limited["gemm_tflops_all_cus"] = round(gflop / (t_all * 1e-6) / 1e12, 1)
+        overlap = {}
+        for n in (32, 64):
+            for op in ("dispatch_bf16", "combine"):
+                dsx = CuLimitedStream(n, dev)
+                gsx = CuLimitedStream(total_cus - n, dev)
+                try:
+                    fn = (lambda i, o=op: run_op(o, i))
+                    window([fn, gemm], [dsx.stream, gsx.stream], [3, 3])          # warm-up
+                    t_d = window([fn], [dsx.stream], [10])[0] / 10
+                    t_g = window([gemm], [gsx.stream], [10])[0] / 10
+                    # Two concurrent rounds: the second sizes both loops by the
+                    # first round's concurrent rates, so that the windows
+                    # cover the same ~20 ms and every call has the other
+                    # stream's work beside it.
+                    nd, ng = max(10, int(20000 / t_d)), max(5, int(20000 / t_g))
+                    both = window([fn, gemm], [dsx.stream, gsx.stream], [nd, ng])
+                    nd = max(10, int(20000 * nd / both[0]))
+                    ng = max(5, int(20000 * ng / both[1]))
+                    both = window([fn, gemm], [dsx.stream, gsx.stream], [nd, ng])
+                    overlap[f"{op}_on_{n}_cus"] = {
+                        "alone_GBps": round(nbytes[op] / (t_d * 1e-6) / 1e9, 1),
+                        "concurrent_GBps": round(nd * nbytes[op] / (both[0] * 1e-6) / 1e9, 1),
+                        "gemm_cus": total_cus - n,
+                        "gemm_alone_tflops": round(gflop / (t_g * 1e-6) / 1e12, 1),
+                        "gemm_concurrent_tflops": round(ng * gflop / (both[1] * 1e-6) / 1e12, 1),
+                        "calls": [nd, ng], "window_us": [round(both[0], 1), round(both[1], 1)],
+                        "window_overlap": round(min(both) / max(both), 3)}
+                finally:
+                    dsx.close()
+                    gsx.close()
+        cu_limited["with_gemm"] = overlap
+        del ga, gb, gc
 
     # Router at the prefill shape, and the decode-time path at 128 tokens
     # (fixed per-expert capacity 128: no slot can be dropped).
@@ -676,6 +759,7 @@ def main():
         "sustained": sustained,
         "context": context,
         "workgroup_sweep_GBps": sweep,
+        "cu_limited": cu_limited,
         "rank_exchange": exchange,
         "router": router,
         "decode": decode,

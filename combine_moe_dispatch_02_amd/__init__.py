@@ -17,7 +17,8 @@ import torch
 from . import _lib
 from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP8_E4M3, MOE_MX_BLOCK,
                    MOE_EP_FP8_BLOCK, MOE_EP_LL_MAX_TOKENS, MOE_EP_MAX_EXPERTS,
-                   MOE_EP_MAX_TOPK, MOE_EP_STATUS_WORDS, MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX,
+                   MOE_EP_MAX_TOPK, MOE_EP_STATUS_WORDS, MOE_EP_XCDS, MOE_SCORE_SIGMOID,
+                   MOE_SCORE_SOFTMAX,
                    MoeConfig, MoeError, MoeLayoutView, MoeLlView, MoeRankLayoutView)
 
 __all__ = ["Handle", "MoeError", "MoeConfig", "moe_workspace_bytes", "moe_handle_create",
@@ -26,6 +27,8 @@ __all__ = ["Handle", "MoeError", "MoeConfig", "moe_workspace_bytes", "moe_handle
            "moe_combine_ranks", "moe_set_max_workgroups", "moe_route", "moe_layout_dispatch",
            "moe_ll_dispatch",
            "moe_ll_view", "moe_ll_combine", "moe_status_string", "moe_last_error",
+           "moe_cu_mask", "moe_stream_create_cu_limited", "moe_stream_destroy", "CuLimitedStream",
+           "MOE_EP_XCDS",
            "MOE_DTYPE_BF16", "MOE_DTYPE_MXFP8_E4M3", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
            "MOE_EP_LL_MAX_TOKENS",
            "MOE_DTYPE_FP8_E4M3", "MOE_EP_MAX_EXPERTS", "MOE_EP_MAX_TOPK", "MOE_EP_FP8_BLOCK"]
@@ -288,6 +291,66 @@ def moe_ll_combine(h: int, y: torch.Tensor, w: torch.Tensor, out: torch.Tensor,
     _lib.check(_lib.load().moe_ll_combine(ctypes.c_void_p(h), ctypes.c_void_p(py), y.shape[0],
                                           ctypes.c_void_p(pw), ctypes.c_void_p(po),
                                           _stream(stream, y.device)))
+
+
+def moe_cu_mask(total_cus: int, num_cus: int) -> list[int]:
+    """The compute-unit mask moe_stream_create_cu_limited uses: num_cus of
+    total_cus units, an equal share of every XCD (host only)."""
+    words = (int(total_cus) + 31) // 32
+    mask = (ctypes.c_uint32 * max(words, 1))()
+    _lib.check(_lib.load().moe_cu_mask(int(total_cus), int(num_cus), mask, words))
+    return list(mask)[:words]
+
+
+def moe_stream_create_cu_limited(num_cus: int) -> int:
+    """A raw hipStream_t (int) on the current device limited to num_cus compute units."""
+    s = ctypes.c_void_p()
+    _lib.check(_lib.load().moe_stream_create_cu_limited(int(num_cus), ctypes.byref(s)))
+    return int(s.value)
+
+
+def moe_stream_destroy(stream: int) -> None:
+    _lib.check(_lib.load().moe_stream_destroy(ctypes.c_void_p(int(stream))))
+
+
+class CuLimitedStream:
+    """A stream whose kernels may use only num_cus compute units (an equal
+    share of every XCD), as a torch stream: ``with CuLimitedStream(64) as s:``
+    makes it torch's current stream, so the Handle calls and torch ops inside
+    run on those units. The stream is synchronised and destroyed on exit (or
+    by close())."""
+
+    def __init__(self, num_cus: int, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        with torch.cuda.device(self.device):
+            self._raw = moe_stream_create_cu_limited(num_cus)
+        self.num_cus = int(num_cus)
+        self.stream = torch.cuda.ExternalStream(self._raw, device=self.device)
+        self._ctx = None
+
+    def __enter__(self):
+        self._ctx = torch.cuda.stream(self.stream)
+        self._ctx.__enter__()
+        return self.stream
+
+    def __exit__(self, *exc):
+        self._ctx.__exit__(*exc)
+        self._ctx = None
+        self.close()
+        return False
+
+    def close(self):
+        if self._raw:
+            self.stream.synchronize()
+            moe_stream_destroy(self._raw)
+            self._raw = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:   # interpreter shutdown: the runtime may be gone
+            pass
 
 
 def moe_status_string(status: int) -> str:

@@ -20,6 +20,7 @@ MOE_EP_MAX_TOPK = 32
 MOE_EP_FP8_BLOCK = 128
 MOE_EP_STATUS_WORDS = 4
 MOE_EP_LL_MAX_TOKENS = 1024
+MOE_EP_XCDS = 8
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
 
@@ -29,7 +30,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_handle_create", "moe_handle_destroy",
            "moe_rank_layout", "moe_rank_layout_view", "moe_dispatch_ranks", "moe_combine_ranks",
            "moe_set_max_workgroups", "moe_route", "moe_layout_dispatch", "moe_ll_dispatch",
            "moe_ll_view",
-           "moe_ll_combine", "moe_status_string", "moe_last_error")
+           "moe_ll_combine", "moe_cu_mask", "moe_stream_create_cu_limited", "moe_stream_destroy",
+           "moe_status_string", "moe_last_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -103,6 +105,9 @@ def load() -> ctypes.CDLL:
         "moe_ll_dispatch": (ctypes.c_int, [vp, vp, i32, i32, vp, ctypes.c_int, vp, vp, i64, vp]),
         "moe_ll_view": (ctypes.c_int, [vp, ctypes.POINTER(MoeLlView)]),
         "moe_ll_combine": (ctypes.c_int, [vp, vp, i64, vp, vp, vp]),
+        "moe_cu_mask": (ctypes.c_int, [i32, i32, ctypes.POINTER(ctypes.c_uint32), i32]),
+        "moe_stream_create_cu_limited": (ctypes.c_int, [i32, ctypes.POINTER(vp)]),
+        "moe_stream_destroy": (ctypes.c_int, [vp]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
     }

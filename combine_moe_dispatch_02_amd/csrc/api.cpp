@@ -414,6 +414,57 @@ int moe_set_max_workgroups(moe_handle_t h, int32_t max_workgroups) {
   return ok();
 }
 
+int moe_cu_mask(int32_t total_cus, int32_t num_cus, uint32_t* mask, int32_t mask_words) {
+  if (mask == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_cu_mask: mask is NULL");
+  const int32_t per = total_cus / MOE_EP_XCDS;   // compute units per XCD
+  if (total_cus <= 0 || total_cus % MOE_EP_XCDS != 0 || per % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_cu_mask: total_cus=%d must be %d XCDs times a multiple of 8 compute units",
+                total_cus, MOE_EP_XCDS);
+  if (num_cus < MOE_EP_XCDS || num_cus > total_cus || num_cus % MOE_EP_XCDS != 0)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_cu_mask: num_cus=%d must be a multiple of %d in [%d, %d] (an equal share of "
+                "every XCD)", num_cus, MOE_EP_XCDS, MOE_EP_XCDS, total_cus);
+  if (int64_t(mask_words) * 32 < total_cus)
+    return fail(MOE_ERR_INVALID_ARG, "moe_cu_mask: mask_words=%d cannot hold %d bits", mask_words,
+                total_cus);
+  for (int32_t i = 0; i < mask_words; ++i) mask[i] = 0u;
+  // Bit b = per*x + 8*((x + q/8) % (per/8)) + (x + q) % 8 for XCD share x and
+  // q = 0 .. num_cus/XCDS - 1. Whether the driver assigns bit b to XCD b % 8
+  // (interleaved) or to XCD b / per (contiguous), every XCD gets exactly
+  // num_cus / XCDS bits, and so does the complement; with the interleaved
+  // assignment each XCD's bits also cycle through its shader engines.
+  const int32_t m = num_cus / MOE_EP_XCDS, groups = per / 8;
+  for (int32_t x = 0; x < MOE_EP_XCDS; ++x)
+    for (int32_t q = 0; q < m; ++q) {
+      const int32_t b = per * x + 8 * ((x + q / 8) % groups) + (x + q) % 8;
+      mask[b / 32] |= 1u << (b % 32);
+    }
+  return ok();
+}
+
+int moe_stream_create_cu_limited(int32_t num_cus, hipStream_t* out) {
+  if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_stream_create_cu_limited: out is NULL");
+  int dev = 0, total = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&total, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return hip_status(err, "moe_stream_create_cu_limited");
+  uint32_t mask[64];
+  if (total > 64 * 32)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_stream_create_cu_limited: %d compute units", total);
+  const int words = (total + 31) / 32;
+  const int st = moe_cu_mask(total, num_cus, mask, words);
+  if (st != MOE_OK) return st;
+  err = hipExtStreamCreateWithCUMask(out, static_cast<uint32_t>(words), mask);
+  if (err != hipSuccess) return hip_status(err, "moe_stream_create_cu_limited");
+  return ok();
+}
+
+int moe_stream_destroy(hipStream_t stream) {
+  if (stream == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_stream_destroy: stream is NULL");
+  return hip_status(hipStreamDestroy(stream), "moe_stream_destroy");
+}
+
 int moe_route(moe_handle_t h, const float* d_logits, int32_t num_tokens, int score,
               int32_t* d_topk_idx, float* d_topk_w, hipStream_t stream) {
   if (h == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_route: handle is NULL");

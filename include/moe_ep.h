@@ -4,10 +4,10 @@
  *
  * What the operations are, per the source pages:
  *   - "Inside the Nebius + PyTorch DeepSeek V3 recipe", section
- *     "Mixture-of-experts and wide expert parallelism": each MoE layer has a
- *     dispatch phase that sends every token to the experts its router chose,
- *     and a combine phase that returns the expert outputs to the tokens'
- *     original positions.
+ *     "Mixture-of-experts and wide expert parallelism": each MoE layer
+ *     exchanges tokens twice -- dispatch moves every token to the experts its
+ *     router chose, and combine brings each expert's output back to the place
+ *     of the token it belongs to.
  *   - Hybrid-EP news item, "Technical Structure": the library's two core
  *     operators are dispatch and combine; "Availability and Integration":
  *     buffers are preallocated for the worst case because routing is dynamic.
@@ -68,6 +68,7 @@ extern "C" {
 #define MOE_EP_FP8_BLOCK 128
 #define MOE_EP_STATUS_WORDS 4
 #define MOE_EP_LL_MAX_TOKENS 1024 /* num_tokens limit of the decode-time calls */
+#define MOE_EP_XCDS 8             /* accelerator dies (XCDs) of an MI355X; CU masks split evenly */
 
 typedef enum {
   MOE_OK = 0,
@@ -228,6 +229,37 @@ int moe_combine_ranks(moe_handle_t h, const void* d_y, int64_t y_rows, void* d_o
  * Numbers"). Results are bit-identical for every cap. Negative values are
  * MOE_ERR_INVALID_ARG. Host-side only; enqueues nothing. */
 int moe_set_max_workgroups(moe_handle_t h, int32_t max_workgroups);
+
+/* ---- Compute-unit-limited streams -------------------------------------------
+ * The Hybrid-EP news item ("Efficiency Numbers") makes the point that the
+ * exchange should need only a few SMs (4 fill NVLink), leaving the rest of
+ * the GPU to the expert computation. Here the caller runs dispatch and
+ * combine on a stream whose kernels may only use num_cus compute units, and
+ * its other work (an expert GEMM) on a stream limited to the complement.
+ *
+ * The hardware spreads a kernel's workgroups over the MI355X's 8 XCDs in
+ * turn, so a mask must leave every XCD some compute units (an XCD with none
+ * would hold its share of the workgroups forever). moe_cu_mask gives each XCD
+ * num_cus / MOE_EP_XCDS bits whether the driver maps mask bit b to XCD b % 8
+ * or to XCD b / (total_cus / 8), and the complement likewise. */
+
+/* Fill mask[0 .. mask_words) (bit b of word b/32 = compute unit b) with
+ * num_cus compute units out of total_cus, an equal share of every XCD.
+ * total_cus: MOE_EP_XCDS times a multiple of 8; num_cus: a multiple of
+ * MOE_EP_XCDS in [MOE_EP_XCDS, total_cus]; mask_words * 32 >= total_cus.
+ * Host only: touches no device. */
+int moe_cu_mask(int32_t total_cus, int32_t num_cus, uint32_t* mask, int32_t mask_words);
+
+/* Create a stream on the current device whose kernels may use only the
+ * num_cus compute units of moe_cu_mask(device CU count, num_cus)
+ * (hipExtStreamCreateWithCUMask; the stream has the default priority).
+ * Release it with moe_stream_destroy. A CU-limited stream has a hardware
+ * queue of its own, so keep few of them alive at once. */
+int moe_stream_create_cu_limited(int32_t num_cus, hipStream_t* out);
+
+/* Destroy a stream made by moe_stream_create_cu_limited (after its work is
+ * done: hipStreamDestroy semantics). */
+int moe_stream_destroy(hipStream_t stream);
 
 /* Router: top-k expert selection and combine weights, the step that produces
  * topk_idx / topk_w for the layout calls. Each token activates the top-k of

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function(lib):
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ("MOE_EP_MAX_EXPERTS", "MOE_EP_MAX_TOPK", "MOE_EP_FP8_BLOCK", "MOE_EP_STATUS_WORDS",
-                 "MOE_EP_LL_MAX_TOKENS"):
+                 "MOE_EP_LL_MAX_TOKENS", "MOE_EP_XCDS"):
         m = re.search(rf"#define {name} (\d+)", text)
         assert m and int(m.group(1)) == getattr(_lib, name)
     for name in ("MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_STATE", "MOE_ERR_HIP",
@@ -276,3 +276,51 @@ def test_binding_shape_check():
         _matrix(t, "t", 4, 7)
     with pytest.raises(ValueError, match="matrix"):
         _matrix(torch.empty(24), "t", 4)
+
+
+# ---------------------------------------------------------------- CU masks
+
+def _mask_bits(lib, total, n):
+    words = (total + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    assert lib.moe_cu_mask(total, n, mask, words) == _lib.MOE_OK, lib.moe_last_error()
+    return [b for b in range(total) if mask[b // 32] >> (b % 32) & 1]
+
+
+@pytest.mark.parametrize("total", [256, 128, 512])
+def test_cu_mask_gives_every_xcd_an_equal_share(lib, total):
+    """Whether the driver assigns mask bit b to XCD b % 8 (interleaved) or to
+    XCD b // (total / 8) (contiguous), every XCD gets n / 8 of the n bits and
+    (total - n) / 8 of the rest; none is left without a compute unit."""
+    per = total // 8
+    for n in range(8, total + 1, 8):
+        bits = _mask_bits(lib, total, n)
+        assert len(bits) == n
+        rest = sorted(set(range(total)) - set(bits))
+        for chosen, want in ((bits, n // 8), (rest, (total - n) // 8)):
+            assert [sum(1 for b in chosen if b % 8 == x) for x in range(8)] == [want] * 8
+            assert [sum(1 for b in chosen if b // per == x) for x in range(8)] == [want] * 8
+
+
+def test_cu_mask_spreads_over_shader_engines(lib):
+    """With the interleaved assignment, bit b lands in shader engine (b // 8) % 4
+    of its XCD; from 4 units per XCD on, every engine of every XCD gets some."""
+    for n in (32, 64, 128, 256):
+        bits = _mask_bits(lib, 256, n)
+        for x in range(8):
+            engines = {(b // 8) % 4 for b in bits if b % 8 == x}
+            assert engines == {0, 1, 2, 3}, (n, x, engines)
+
+
+def test_cu_mask_rejects_bad_arguments(lib):
+    mask = (ctypes.c_uint32 * 8)()
+    assert lib.moe_cu_mask(256, 12, mask, 8) == _lib.MOE_ERR_INVALID_ARG   # not a multiple of 8
+    assert lib.moe_cu_mask(256, 0, mask, 8) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_cu_mask(256, 264, mask, 8) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_cu_mask(256, 64, mask, 7) == _lib.MOE_ERR_INVALID_ARG    # too few words
+    assert lib.moe_cu_mask(256, 64, None, 8) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_cu_mask(260, 64, mask, 9) == _lib.MOE_ERR_UNSUPPORTED    # not 8 equal XCDs
+    assert lib.moe_cu_mask(200, 64, mask, 8) == _lib.MOE_ERR_UNSUPPORTED    # 25 per XCD
+    assert b"XCD" in lib.moe_last_error()
+    assert lib.moe_stream_create_cu_limited(64, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_destroy(None) == _lib.MOE_ERR_INVALID_ARG
