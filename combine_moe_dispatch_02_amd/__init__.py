@@ -22,7 +22,8 @@ from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP8_E4M3, MOE
                    MoeConfig, MoeError, MoeLayoutView, MoeLlView, MoeRankLayoutView)
 
 __all__ = ["Handle", "MoeError", "MoeConfig", "moe_workspace_bytes", "moe_handle_create",
-           "moe_handle_destroy", "moe_dispatch_layout", "moe_layout_view", "moe_dispatch",
+           "moe_handle_destroy", "moe_dispatch_layout", "moe_dispatch_layout_noalloc",
+           "moe_layout_view", "moe_dispatch",
            "moe_combine", "moe_rank_layout", "moe_rank_layout_view", "moe_dispatch_ranks",
            "moe_combine_ranks", "moe_set_max_workgroups", "moe_route", "moe_layout_dispatch",
            "moe_ll_dispatch",
@@ -130,6 +131,30 @@ def moe_dispatch_layout(h: int, topk_idx: torch.Tensor, stream=None) -> None:
         _matrix(topk_idx, "topk_idx", cfg.topk)
     _lib.check(_lib.load().moe_dispatch_layout(ctypes.c_void_p(h), ctypes.c_void_p(p),
                                                topk_idx.shape[0], _stream(stream, topk_idx.device)))
+
+
+def moe_dispatch_layout_noalloc(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                                pos: torch.Tensor, src_idx: torch.Tensor, counts_e: torch.Tensor,
+                                offsets_e: torch.Tensor, counts_r: torch.Tensor,
+                                offsets_r: torch.Tensor, status: torch.Tensor, stream=None) -> None:
+    """The layout into caller-owned int32 tensors, with no handle, workspace or
+    allocation (its histograms live in the library's static device array)."""
+    T, k = (int(topk_idx.shape[0]), int(topk_idx.shape[1])) if topk_idx.dim() == 2 else (-1, -1)
+    if T < 0:
+        raise ValueError(f"topk_idx must be [num_tokens, topk], got shape {tuple(topk_idx.shape)}")
+    dev = topk_idx.device
+    want = {"pos": (pos, T * k), "src_idx": (src_idx, T * k), "counts_e": (counts_e, num_experts),
+            "offsets_e": (offsets_e, num_experts + 1), "counts_r": (counts_r, num_ranks),
+            "offsets_r": (offsets_r, num_ranks + 1), "status": (status, MOE_EP_STATUS_WORDS)}
+    ptrs = {}
+    for name, (t, n) in want.items():
+        ptrs[name] = _ptr(t, torch.int32, name, dev)
+        if t.numel() < n:
+            raise ValueError(f"{name} has {t.numel()} entries; this call writes {n}")
+    pi = _ptr(topk_idx, torch.int32, "topk_idx", dev)
+    _lib.check(_lib.load().moe_dispatch_layout_noalloc(
+        ctypes.c_void_p(pi), T, k, int(num_experts), int(num_ranks),
+        *(ctypes.c_void_p(ptrs[n]) for n in want), _stream(stream, dev)))
 
 
 def moe_layout_view(h: int) -> MoeLayoutView:

@@ -21,12 +21,14 @@ MOE_EP_FP8_BLOCK = 128
 MOE_EP_STATUS_WORDS = 4
 MOE_EP_LL_MAX_TOKENS = 1024
 MOE_EP_XCDS = 8
+MOE_EP_NOALLOC_SCRATCH_BYTES = 2 << 20
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
 
 # Every function the header declares, for the export check.
 EXPORTS = ("moe_workspace_bytes", "moe_handle_create", "moe_handle_destroy",
-           "moe_dispatch_layout", "moe_layout_view", "moe_dispatch", "moe_combine",
+           "moe_dispatch_layout", "moe_dispatch_layout_noalloc", "moe_layout_view", "moe_dispatch",
+           "moe_combine",
            "moe_rank_layout", "moe_rank_layout_view", "moe_dispatch_ranks", "moe_combine_ranks",
            "moe_set_max_workgroups", "moe_route", "moe_layout_dispatch", "moe_ll_dispatch",
            "moe_ll_view",
@@ -92,6 +94,8 @@ def load() -> ctypes.CDLL:
         "moe_handle_create": (ctypes.c_int, [cfgp, vp, sz, ctypes.POINTER(vp)]),
         "moe_handle_destroy": (None, [vp]),
         "moe_dispatch_layout": (ctypes.c_int, [vp, vp, i32, vp]),
+        "moe_dispatch_layout_noalloc": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, vp,
+                                                       vp, vp, vp, vp]),
         "moe_layout_view": (ctypes.c_int, [vp, ctypes.POINTER(MoeLayoutView)]),
         "moe_dispatch": (ctypes.c_int, [vp, vp, ctypes.c_int, vp, vp, i64, vp]),
         "moe_combine": (ctypes.c_int, [vp, vp, i64, vp, vp, vp]),

@@ -253,6 +253,43 @@ int moe_dispatch_layout(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_t
   return ok();
 }
 
+int moe_dispatch_layout_noalloc(const int32_t* d_topk_idx, int32_t num_tokens, int32_t topk,
+                                int32_t num_experts, int32_t num_ranks, int32_t* d_pos,
+                                int32_t* d_src_idx, int32_t* d_counts_e, int32_t* d_offsets_e,
+                                int32_t* d_counts_r, int32_t* d_offsets_r, int32_t* d_status,
+                                hipStream_t stream) {
+  const char* fn = "moe_dispatch_layout_noalloc";
+  if (num_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "%s: num_tokens=%d must be >= 0", fn, num_tokens);
+  const moe_config_t c{num_tokens, 8, topk, num_experts, num_ranks};   // hidden plays no part
+  const int st = check_config(&c);
+  if (st != MOE_OK) return st;
+  if (d_counts_e == nullptr || d_offsets_e == nullptr || d_counts_r == nullptr ||
+      d_offsets_r == nullptr || d_status == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "%s: counts, offsets and status must not be NULL", fn);
+  if (num_tokens > 0 && (d_topk_idx == nullptr || d_pos == nullptr || d_src_idx == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_idx, pos and src_idx must not be NULL", fn);
+  for (const void* p : {static_cast<const void*>(d_topk_idx), static_cast<const void*>(d_pos),
+                        static_cast<const void*>(d_src_idx), static_cast<const void*>(d_counts_e),
+                        static_cast<const void*>(d_offsets_e), static_cast<const void*>(d_counts_r),
+                        static_cast<const void*>(d_offsets_r), static_cast<const void*>(d_status)})
+    if (!aligned(p, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: arrays must be 4-byte aligned", fn);
+  const size_t need = moe::layout_scratch_ints(num_tokens, topk, num_experts);
+  if (need > moe::kNoallocScratchInts)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: %d tokens x top-%d over %d experts need %zu bytes of histogram scratch; the "
+                "static array holds %zu: lay out fewer tokens per call, or use "
+                "moe_dispatch_layout with a workspace",
+                fn, num_tokens, topk, num_experts, need * sizeof(int32_t),
+                size_t(MOE_EP_NOALLOC_SCRATCH_BYTES));
+  int32_t* scratch = nullptr;
+  hipError_t err = moe::layout_scratch(&scratch);
+  if (err != hipSuccess) return hip_status(err, fn);
+  const moe::LayoutArrays a{d_status, d_counts_e, d_offsets_e, d_counts_r, d_offsets_r,
+                            scratch,  d_pos,      d_src_idx};
+  err = moe::launch_layout(d_topk_idx, num_tokens, topk, num_experts, num_ranks, a, stream);
+  return hip_status(err, fn);
+}
+
 int moe_layout_view(moe_handle_t h, moe_layout_view_t* out) {
   if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "moe_layout_view: out is NULL");
   const int st = check_ready(h, "moe_layout_view");

@@ -28,6 +28,8 @@
 // ceil(log2 E) ballots (one per id bit); the lowest lane of each group does
 // the single LDS update for the group, and every lane's rank inside its group
 // is the number of group lanes below it (mbcnt).
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -364,6 +366,42 @@ hipError_t launch_layout(const int32_t* d_idx, int num_tokens, int topk, int num
   LayoutOut o{a.hist, a.counts_e, a.offsets_e, a.counts_r, a.offsets_r, a.pos, a.src_idx,
               a.status, nullptr, num_ranks, per};
   return launch_pass<false>(b, o, stream);
+}
+
+// ---- Layout without a workspace ---------------------------------------------
+// The per-workgroup histograms of moe_dispatch_layout_noalloc live in this
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in for the symbol): layout_scratch() looks up its device address
+// once per device, with that device current, and the kernels take that
+// pointer. Every call on a GPU shares its copy; the histogram kernel writes
+// every entry the place kernel then reads, so nothing needs clearing between
+// calls, and calls that overlap on one GPU race.
+static __device__ __align__(256) int32_t g_layout_scratch[kNoallocScratchInts];
+
+hipError_t layout_scratch(int32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static int32_t* ptr[kMaxDevices];
+  static hipError_t err[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(g_layout_scratch));
+    ptr[dev] = err[dev] == hipSuccess ? static_cast<int32_t*>(p) : nullptr;
+  });
+  if (err[dev] != hipSuccess) return err[dev];
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+size_t layout_scratch_ints(int num_tokens, int topk, int num_experts) {
+  const int64_t slots = int64_t(num_tokens) * topk;
+  if (slots <= kLayoutSingleChunk) return 0;   // one workgroup, no histograms
+  return static_cast<size_t>(layout_blocks(slots)) * static_cast<size_t>(num_experts);
 }
 
 hipError_t launch_rank_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,

@@ -60,6 +60,18 @@ struct RankArrays {
   int32_t* src;       // [T_max * min(k, R)] token of each row
 };
 
+// moe_dispatch_layout_noalloc: capacity of the static histogram array, in
+// int32 entries (MOE_EP_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kNoallocScratchInts = MOE_EP_NOALLOC_SCRATCH_BYTES / sizeof(int32_t);
+
+// Device address of this GPU's static histogram array (looked up on the first
+// call on each device, with that device current).
+hipError_t layout_scratch(int32_t** out);
+
+// Histogram entries a layout of num_tokens x topk slots over num_experts
+// needs (0 when one workgroup does it all).
+size_t layout_scratch_ints(int num_tokens, int topk, int num_experts);
+
 // Host-side launchers; each returns the hipError_t of its launches.
 hipError_t launch_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,
                          int num_ranks, const LayoutArrays& a, hipStream_t stream);

@@ -69,6 +69,7 @@ extern "C" {
 #define MOE_EP_STATUS_WORDS 4
 #define MOE_EP_LL_MAX_TOKENS 1024 /* num_tokens limit of the decode-time calls */
 #define MOE_EP_XCDS 8             /* accelerator dies (XCDs) of an MI355X; CU masks split evenly */
+#define MOE_EP_NOALLOC_SCRATCH_BYTES (2u << 20) /* per-GPU static scratch of the no-alloc layout */
 
 typedef enum {
   MOE_OK = 0,
@@ -139,6 +140,33 @@ int moe_dispatch_layout(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_t
 
 /* Device pointers and sizes of the last layout (MOE_ERR_STATE before one). */
 int moe_layout_view(moe_handle_t h, moe_layout_view_t* out);
+
+/* Layout that allocates nothing and needs no handle or workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Computes exactly what
+ * moe_dispatch_layout computes for a handle with this topk, num_experts and
+ * num_ranks, into caller-owned device arrays: d_pos [num_tokens * topk],
+ * d_src_idx [num_tokens * topk], d_counts_e [num_experts], d_offsets_e
+ * [num_experts + 1], d_counts_r [num_ranks], d_offsets_r [num_ranks + 1],
+ * d_status [MOE_EP_STATUS_WORDS] (all int32, 4-byte aligned; d_topk_idx,
+ * d_pos and d_src_idx may be NULL when num_tokens is 0). The layout's
+ * per-workgroup histograms go to a static device array of
+ * MOE_EP_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends:
+ * ceil(num_tokens * topk / 1024) * num_experts * 4 bytes must fit in it (e.g.
+ * 2,097,152 slots at 256 experts; no histograms at all up to 4096 slots),
+ * else MOE_ERR_UNSUPPORTED and nothing is enqueued. The configuration limits
+ * are moe_handle_create's. Every call on one GPU shares that GPU's array, so
+ * calls that may overlap on one GPU (other streams, other threads) race:
+ * order them on one stream. The first call on each device looks the array up
+ * (no allocation); no call allocates or frees memory. Enqueued on `stream`,
+ * no host synchronisation. The results feed dispatch and combine only through
+ * a handle's layout (moe_dispatch_layout); this call is for callers that
+ * consume pos / offsets themselves. */
+int moe_dispatch_layout_noalloc(const int32_t* d_topk_idx, int32_t num_tokens, int32_t topk,
+                                int32_t num_experts, int32_t num_ranks, int32_t* d_pos,
+                                int32_t* d_src_idx, int32_t* d_counts_e, int32_t* d_offsets_e,
+                                int32_t* d_counts_r, int32_t* d_offsets_r, int32_t* d_status,
+                                hipStream_t stream);
 
 /* Dispatch: scatter token rows into the expert-major buffer.
  * d_x: bf16 [num_tokens, hidden]. out_rows >= capacity of the last layout.
