@@ -132,7 +132,7 @@ def queue_ahead():
         _QUEUE_AHEAD_BUF.fill_(i)
 
 
-KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_slots_kernel",
+KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_slots_kernel<2>",
                 "dispatch_fp8": "dispatch_fp8_kernel", "combine": "combine_kernel<true>"}
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "traffic_deepseekv3.json")

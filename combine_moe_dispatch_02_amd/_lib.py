@@ -86,7 +86,12 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m combine_moe_dispatch_02_amd.build` (or __graft_entry__.build())")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Set the argument and result types of every exported function on `lib`."""
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     cfgp = ctypes.POINTER(MoeConfig)
     sig = {
@@ -119,7 +124,6 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
 
 

@@ -37,22 +37,30 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; install ROCm or set HIPCC")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into one shared library next to this file."""
+# Host-side AddressSanitizer build (a check of the C ABI's host code; the GPU
+# code is built as usual): each -fsanitize= applies to the host pass only.
+HOST_ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+                   "-g"]
+
+
+def build(verbose: bool = False, out: str = LIB_PATH, host_asan: bool = False) -> str:
+    """Compile every source into one shared library (next to this file unless
+    `out` says otherwise; with host_asan, the host code is instrumented)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-x", "hip", *srcs, "-o", tmp]
+    tmp = out + ".tmp"
+    flags = HIPCC_FLAGS + (HOST_ASAN_FLAGS if host_asan else [])
+    cmd = [hipcc(), *flags, "-I", INCLUDE, "-I", CSRC, "-x", "hip", *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         # never leave a library built from older sources in place
-        for stale in (LIB_PATH, tmp):
+        for stale in (out, tmp):
             if os.path.exists(stale):
                 os.remove(stale)
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -382,10 +382,11 @@ constexpr int kSlotsPerWave = 2;
 // 5570-5582, 1024 5556-5610 / 5466-5617. So the loop below 512 workgroups.
 constexpr int kSlotsFormMinCap = 512;
 
-// Slots a wavefront of the slot-spread form stores: at most
-// ceil(MOE_EP_MAX_TOPK / kSlotWaves).
+// Slots a wavefront of the slot-spread form stores: kSlotsPerWave up to
+// k = 2 * kSlotWaves, at most ceil(MOE_EP_MAX_TOPK / kSlotWaves) beyond.
 constexpr int kMaxSlotsPerWave = (MOE_EP_MAX_TOPK + kSlotWaves - 1) / kSlotWaves;
 
+template <int kPer>
 __global__ __launch_bounds__(64 * kSlotWaves) void dispatch_bf16_slots_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, int topk, int64_t rows,
     u32x4* __restrict__ out, int num_tokens, int nvec, int slices, int payload_blocks) {
@@ -404,20 +405,20 @@ __global__ __launch_bounds__(64 * kSlotWaves) void dispatch_bf16_slots_kernel(
     // added its own latency to the wavefront's.
     // Unconditional loads (slot indices clamped to k-1) so that they issue
     // back to back; slots past k are then dropped.
-    int p[kMaxSlotsPerWave];
+    int p[kPer];
 #pragma unroll
-    for (int i = 0; i < kMaxSlotsPerWave; ++i) {
+    for (int i = 0; i < kPer; ++i) {
       const int j = w + i * waves;
       p[i] = table_row(pos, topk, rows, t, j < topk ? j : topk - 1);
     }
 #pragma unroll
-    for (int i = 0; i < kMaxSlotsPerWave; ++i)
+    for (int i = 0; i < kPer; ++i)
       if (w + i * waves >= topk) p[i] = -1;
     u32x4 r = {0u, 0u, 0u, 0u};
     if (active) r = x[static_cast<size_t>(t) * nvec + v];
     loaded(r);
 #pragma unroll
-    for (int i = 0; i < kMaxSlotsPerWave; ++i)
+    for (int i = 0; i < kPer; ++i)
       if (p[i] >= 0 && active) store_row(&out[static_cast<size_t>(p[i]) * nvec + v], r);
   }
 }
@@ -892,18 +893,25 @@ hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, voi
     // kItemWaves.
     const int want = (topk + kSlotsPerWave - 1) / kSlotsPerWave;
     const int waves = want < kSlotWaves ? want : kSlotWaves;
-    // Every slot belongs to one of the waves' kMaxSlotsPerWave entries
-    // (topk <= MOE_EP_MAX_TOPK, checked at handle creation).
-    if (waves * kMaxSlotsPerWave < topk) return hipErrorInvalidValue;
+    // Every slot belongs to one of the waves' entries (topk <= MOE_EP_MAX_TOPK,
+    // checked at handle creation): kSlotsPerWave each while waves covers
+    // ceil(k / 2), kMaxSlotsPerWave once waves is capped at kSlotWaves.
+    const int per = waves * kSlotsPerWave >= topk ? kSlotsPerWave : kMaxSlotsPerWave;
+    if (waves * per < topk) return hipErrorInvalidValue;
     int64_t blocks = int64_t(num_tokens) * slices;
     if (max_blocks > 0) {
       int64_t cap = int64_t(max_blocks) * kItemWaves / waves;
       if (cap < 1) cap = 1;
       if (blocks > cap) blocks = cap;
     }
-    hipLaunchKernelGGL(dispatch_bf16_slots_kernel, dim3(static_cast<unsigned>(blocks)),
-                       dim3(64 * waves), 0, stream, x, d_pos, topk, rows, out, num_tokens,
-                       hidden / 8, slices, static_cast<int>(blocks));
+    if (per == kSlotsPerWave)
+      hipLaunchKernelGGL(dispatch_bf16_slots_kernel<kSlotsPerWave>,
+                         dim3(static_cast<unsigned>(blocks)), dim3(64 * waves), 0, stream, x, d_pos,
+                         topk, rows, out, num_tokens, hidden / 8, slices, static_cast<int>(blocks));
+    else
+      hipLaunchKernelGGL(dispatch_bf16_slots_kernel<kMaxSlotsPerWave>,
+                         dim3(static_cast<unsigned>(blocks)), dim3(64 * waves), 0, stream, x, d_pos,
+                         topk, rows, out, num_tokens, hidden / 8, slices, static_cast<int>(blocks));
   } else if (dtype == MOE_DTYPE_FP8_E4M3)
     hipLaunchKernelGGL(dispatch_fp8_kernel, grid, block, 0, stream, x, d_pos, topk, rows, out,
                        static_cast<float*>(d_scales), num_tokens, hidden, slices, payload);
