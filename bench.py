@@ -507,7 +507,8 @@ def main():
     # dispatch and combine on n units concurrently with a bf16 GEMM
     # (8192 x 8192 x 8192, torch) on a stream limited to the other 256 - n.
     cu_limited = {}
-    if args.sustained_iters > 0 and "cus" not in skip:
+
+    def measure_cu_limited():
         from combine_moe_dispatch_02_amd import CuLimitedStream
         total_cus = torch.cuda.get_device_properties(dev).multi_processor_count
         by_cus = {}
@@ -581,6 +582,15 @@ def main():
                     gsx.close()
         cu_limited["with_gemm"] = overlap
         del ga, gb, gc
+
+    if args.sustained_iters > 0 and "cus" not in skip:
+        # A box whose runtime refuses CU-masked streams still reports the rest.
+        from combine_moe_dispatch_02_amd import MoeError
+        try:
+            measure_cu_limited()
+        except (MoeError, RuntimeError) as e:
+            torch.cuda.synchronize()
+            cu_limited["error"] = f"{type(e).__name__}: {e}"
 
     # Router at the prefill shape, and the decode-time path at 128 tokens
     # (fixed per-expert capacity 128: no slot can be dropped).
