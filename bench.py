@@ -529,26 +529,46 @@ def main():
         def gemm(i):
             torch.mm(ga, gb, out=gc)
 
-        def window(calls, streams, counts):
-            """Run calls[s](i) for i < counts[s] on each stream, interleaved in
-            issue order; returns each stream's elapsed us (HIP events)."""
-            evs = [(HipTimer(), HipTimer()) for _ in streams]
-            for (a, _), st in zip(evs, streams):
-                a.record(st)
-            for i in range(max(counts)):
-                for s, st in enumerate(streams):
-                    if i < counts[s]:
-                        with torch.cuda.stream(st):
-                            calls[s](i)
-            for (_, b), st in zip(evs, streams):
-                b.record(st)
+        def loop_us(fn, st, n):
+            """Elapsed us of n back-to-back calls of fn on stream st (HIP events)."""
+            e = (HipTimer(), HipTimer())
+            with torch.cuda.stream(st):
+                e[0].record(st)
+                for i in range(n):
+                    fn(i)
+                e[1].record(st)
             torch.cuda.synchronize()
-            return [a.elapsed_time(b) * 1e3 for a, b in evs]
+            return e[0].elapsed_time(e[1]) * 1e3
+
+        def under_load(inner, st_in, n_in, outer, st_out, n_out):
+            """us of n_in calls of `inner` on st_in while `outer` runs on
+            st_out the whole time: the outer loop is enqueued first and the
+            inner stream spins ~1 ms before its loop, so every inner call has
+            outer work beside it. Returns (inner us, whether the outer loop's
+            events bracket the inner loop's)."""
+            eo = (HipTimer(), HipTimer())
+            ei = (HipTimer(), HipTimer())
+            with torch.cuda.stream(st_out):
+                eo[0].record(st_out)
+                for i in range(n_out):
+                    outer(i)
+                eo[1].record(st_out)
+            with torch.cuda.stream(st_in):
+                sleep = getattr(torch.cuda, "_sleep", None)
+                if sleep is not None:
+                    sleep(2_000_000)
+                ei[0].record(st_in)
+                for i in range(n_in):
+                    inner(i)
+                ei[1].record(st_in)
+            torch.cuda.synchronize()
+            covered = eo[0].elapsed_time(ei[0]) > 0 and ei[1].elapsed_time(eo[1]) > 0
+            return ei[0].elapsed_time(ei[1]) * 1e3, covered
 
         # the GEMM alone on every compute unit, for reference
         for i in range(3):
             gemm(i)
-        t_all = window([gemm], [stream], [20])[0] / 20
+        t_all = loop_us(gemm, stream, 20) / 20
         cu_limited["gemm_tflops_all_cus"] = round(gflop / (t_all * 1e-6) / 1e12, 1)
         overlap = {}
         for n in (32, 64):
@@ -557,27 +577,38 @@ def main():
                 gsx = CuLimitedStream(total_cus - n, dev)
                 try:
                     fn = (lambda i, o=op: run_op(o, i))
-                    window([fn, gemm], [dsx.stream, gsx.stream], [3, 3])          # warm-up
-                    t_d = window([fn], [dsx.stream], [10])[0] / 10
-                    t_g = window([gemm], [gsx.stream], [10])[0] / 10
-                    # Two concurrent rounds: the second sizes both loops by the
-                    # first round's concurrent rates, so that the windows
-                    # cover the same ~20 ms and every call has the other
-                    # stream's work beside it.
-                    nd, ng = max(10, int(20000 / t_d)), max(5, int(20000 / t_g))
-                    both = window([fn, gemm], [dsx.stream, gsx.stream], [nd, ng])
-                    nd = max(10, int(20000 * nd / both[0]))
-                    ng = max(5, int(20000 * ng / both[1]))
-                    both = window([fn, gemm], [dsx.stream, gsx.stream], [nd, ng])
+                    loop_us(fn, dsx.stream, 3)
+                    loop_us(gemm, gsx.stream, 3)
+                    t_d = loop_us(fn, dsx.stream, 10) / 10
+                    t_g = loop_us(gemm, gsx.stream, 10) / 10
+                    # each side measured over ~8 ms of its own calls while the
+                    # other runs over ~6x that (a slowed inner loop still fits)
+                    nd, ng = max(5, int(8000 / t_d)), max(3, int(8000 / t_g))
+                    us_d, cov_d = under_load(fn, dsx.stream, nd, gemm, gsx.stream,
+                                             max(5, int(48000 / t_g)))
+                    us_g, cov_g = under_load(gemm, gsx.stream, ng, fn, dsx.stream,
+                                             max(10, int(48000 / t_d)))
+                    # the same with the exchange's grid capped at 4 workgroups
+                    # of 4 wavefronts per unit, whose wavefronts loop over the
+                    # items: few workgroup launches instead of one per item
+                    h.set_max_workgroups(4 * n)
+                    t_l = loop_us(fn, dsx.stream, 10) / 10
+                    nl = max(5, int(8000 / t_l))
+                    us_l, cov_l = under_load(fn, dsx.stream, nl, gemm, gsx.stream,
+                                             max(5, int(48000 / t_g)))
                     overlap[f"{op}_on_{n}_cus"] = {
                         "alone_GBps": round(nbytes[op] / (t_d * 1e-6) / 1e9, 1),
-                        "concurrent_GBps": round(nd * nbytes[op] / (both[0] * 1e-6) / 1e9, 1),
+                        "beside_gemm_GBps": round(nd * nbytes[op] / (us_d * 1e-6) / 1e9, 1),
                         "gemm_cus": total_cus - n,
                         "gemm_alone_tflops": round(gflop / (t_g * 1e-6) / 1e12, 1),
-                        "gemm_concurrent_tflops": round(ng * gflop / (both[1] * 1e-6) / 1e12, 1),
-                        "calls": [nd, ng], "window_us": [round(both[0], 1), round(both[1], 1)],
-                        "window_overlap": round(min(both) / max(both), 3)}
+                        "gemm_beside_exchange_tflops": round(ng * gflop / (us_g * 1e-6) / 1e12, 1),
+                        "looping_grid": {
+                            "alone_GBps": round(nbytes[op] / (t_l * 1e-6) / 1e9, 1),
+                            "beside_gemm_GBps": round(nl * nbytes[op] / (us_l * 1e-6) / 1e9, 1)},
+                        "calls_measured": [nd, ng, nl],
+                        "fully_overlapped": bool(cov_d and cov_g and cov_l)}
                 finally:
+                    h.set_max_workgroups(0)
                     dsx.close()
                     gsx.close()
         cu_limited["with_gemm"] = overlap

@@ -250,12 +250,13 @@ int moe_combine_ranks(moe_handle_t h, const void* d_y, int64_t y_rows, void* d_o
  * wavefronts, at least one, and below 512 one wavefront per item with all k
  * slots); 0 (the default) launches one wavefront per (token, column slice)
  * item (bf16 dispatch: one workgroup per item). With a cap, each
- * wavefront loops over several (token, column slice) items,
- * so the work occupies fewer compute units and leaves the rest free for
- * kernels on other streams -- the pages' point that the exchange should fill
- * the link with few compute units (Hybrid-EP news item, "Efficiency
- * Numbers"). Results are bit-identical for every cap. Negative values are
- * MOE_ERR_INVALID_ARG. Host-side only; enqueues nothing. */
+ * wavefront loops over several (token, column slice) items, so the exchange
+ * keeps fewer wavefronts resident; which compute units they run on is not
+ * chosen here (moe_stream_create_cu_limited does that). Related to the
+ * pages' point that the exchange should fill the link with few compute
+ * units (Hybrid-EP news item, "Efficiency Numbers"). Results are
+ * bit-identical for every cap. Negative values are MOE_ERR_INVALID_ARG.
+ * Host-side only; enqueues nothing. */
 int moe_set_max_workgroups(moe_handle_t h, int32_t max_workgroups);
 
 /* ---- Compute-unit-limited streams -------------------------------------------
@@ -269,7 +270,13 @@ int moe_set_max_workgroups(moe_handle_t h, int32_t max_workgroups);
  * turn, so a mask must leave every XCD some compute units (an XCD with none
  * would hold its share of the workgroups forever). moe_cu_mask gives each XCD
  * num_cus / MOE_EP_XCDS bits whether the driver maps mask bit b to XCD b % 8
- * or to XCD b / (total_cus / 8), and the complement likewise. */
+ * or to XCD b / (total_cus / 8), and the complement likewise.
+ *
+ * Measured on MI355X (T=4096, H=7168, top-8, inputs from HBM): 32 units move
+ * 1.35 TB/s of bf16 dispatch alone, but beside a bf16 GEMM on the other 224
+ * units about 0.5 TB/s -- the compute units are disjoint, the memory path
+ * beyond them (L2, fabric, last-level cache, HBM) is shared. The GEMM keeps
+ * over 90% of its rate. */
 
 /* Fill mask[0 .. mask_words) (bit b of word b/32 = compute unit b) with
  * num_cus compute units out of total_cus, an equal share of every XCD.
