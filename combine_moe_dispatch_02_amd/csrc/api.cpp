@@ -27,6 +27,7 @@ struct moe_handle {
   bool rank_ready;
   int32_t rank_num_tokens;
   int32_t max_workgroups;  // 0: one workgroup per 4 work items
+  int32_t order_chunks;    // blocked bf16 dispatch: chunks per block of the last layout, 0: none
   // Decode-time (fixed-capacity) state.
   int32_t* ll_pos;     // [min(T_max, LL max) * k]
   int32_t* ll_counts;  // [E]
@@ -64,7 +65,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Region offsets inside the workspace; returns the total size.
 struct Carve {
-  size_t status, counts_e, offsets_e, counts_r, offsets_r, hist, pos, src_idx;
+  size_t status, counts_e, offsets_e, counts_r, offsets_r, hist, pos, src_idx, order;
   size_t r_status, r_counts, r_offsets, r_hist, r_slot_row, r_rank_pos, r_src;
   size_t ll_pos, ll_counts, ll_status;
   size_t total;
@@ -87,6 +88,7 @@ Carve carve(const moe_config_t& c) {
   r.hist = take(sizeof(int32_t) * size_t(moe::layout_blocks(slots)) * c.num_experts);
   r.pos = take(sizeof(int32_t) * size_t(slots));
   r.src_idx = take(sizeof(int32_t) * size_t(slots));
+  r.order = take(sizeof(int2) * size_t(moe::dispatch_order_entries(c.max_tokens, c.topk)));
   const int64_t rank_rows = int64_t(c.max_tokens) * (c.topk < c.num_ranks ? c.topk : c.num_ranks);
   r.r_status = take(sizeof(int32_t) * MOE_EP_STATUS_WORDS);
   r.r_counts = take(sizeof(int32_t) * c.num_ranks);
@@ -171,6 +173,31 @@ int hip_status(hipError_t err, const char* fn) {
   return fail(MOE_ERR_HIP, "%s: HIP error %d (%s)", fn, int(err), hipGetErrorString(err));
 }
 
+// Layout into the handle's workspace; with lists for the blocked bf16
+// dispatch wherever that form applies to the batch.
+hipError_t handle_layout(moe_handle_t h, const int32_t* d_idx, int32_t num_tokens,
+                         hipStream_t stream) {
+  int chunks = moe::dispatch_block_chunks(num_tokens, h->cfg.topk, h->cfg.hidden);
+  if (int64_t(num_tokens) * h->cfg.topk <= moe::kLayoutSingleChunk) chunks = 0;
+  h->order_chunks = 0;
+  const hipError_t err = moe::launch_layout(d_idx, num_tokens, h->cfg.topk, h->cfg.num_experts,
+                                            h->cfg.num_ranks, h->arrays, stream, chunks);
+  if (err == hipSuccess) h->order_chunks = chunks;
+  return err;
+}
+
+// Dispatch through the handle's last layout: the blocked form for bf16 when
+// the layout listed the blocks and no workgroup cap is set, else the forms
+// that read the position table.
+hipError_t handle_dispatch(moe_handle_t h, int dtype, const void* d_x, void* d_out, void* d_scales,
+                           int64_t out_rows, int32_t num_tokens, hipStream_t stream) {
+  if (dtype == MOE_DTYPE_BF16 && h->max_workgroups == 0 && h->order_chunks > 0)
+    return moe::launch_dispatch_blocks(d_x, h->arrays.order, d_out, out_rows, num_tokens,
+                                       h->cfg.topk, h->cfg.hidden, h->order_chunks, stream);
+  return moe::launch_dispatch(dtype, d_x, h->arrays.pos, d_out, d_scales, out_rows, num_tokens,
+                              h->cfg.topk, h->cfg.hidden, h->max_workgroups, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,6 +235,7 @@ int moe_handle_create(const moe_config_t* cfg, void* d_workspace, size_t ws_byte
   h->arrays.hist = at(c.hist);
   h->arrays.pos = at(c.pos);
   h->arrays.src_idx = at(c.src_idx);
+  h->arrays.order = reinterpret_cast<int2*>(h->ws + c.order);
   h->rank.status = at(c.r_status);
   h->rank.counts = at(c.r_counts);
   h->rank.offsets = at(c.r_offsets);
@@ -220,6 +248,7 @@ int moe_handle_create(const moe_config_t* cfg, void* d_workspace, size_t ws_byte
   h->rank_ready = false;
   h->rank_num_tokens = 0;
   h->max_workgroups = 0;
+  h->order_chunks = 0;
   h->ll_pos = at(c.ll_pos);
   h->ll_counts = at(c.ll_counts);
   h->ll_status = at(c.ll_status);
@@ -242,8 +271,7 @@ int moe_dispatch_layout(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_t
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch_layout: topk_idx is NULL");
   if (!aligned(d_topk_idx, 4))
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch_layout: topk_idx must be 4-byte aligned");
-  const hipError_t err = moe::launch_layout(d_topk_idx, num_tokens, h->cfg.topk,
-                                            h->cfg.num_experts, h->cfg.num_ranks, h->arrays, stream);
+  const hipError_t err = handle_layout(h, d_topk_idx, num_tokens, stream);
   if (err != hipSuccess) {
     h->ready = false;
     return hip_status(err, "moe_dispatch_layout");
@@ -331,8 +359,7 @@ int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, void* 
   if (dtype != MOE_DTYPE_BF16 && !aligned(d_scales, 4))
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: scales must be 4-byte aligned");
   const hipError_t err =
-      moe::launch_dispatch(dtype, d_x, h->arrays.pos, d_out, d_scales, out_rows, h->num_tokens,
-                           h->cfg.topk, h->cfg.hidden, h->max_workgroups, stream);
+      handle_dispatch(h, dtype, d_x, d_out, d_scales, out_rows, h->num_tokens, stream);
   return hip_status(err, "moe_dispatch");
 }
 
@@ -557,16 +584,14 @@ int moe_layout_dispatch(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_t
   // 256), and they give the same results.
   hipError_t err;
   if (num_tokens < kLayoutDispatchFusedBelow) {
+    h->order_chunks = 0;   // the one-launch form writes no block lists
     err = moe::launch_layout_dispatch(dtype, d_x, d_topk_idx, num_tokens, h->cfg.topk,
                                       h->cfg.num_experts, h->cfg.num_ranks, h->arrays, d_out,
                                       d_scales, h->cfg.hidden, h->max_workgroups, stream);
   } else {
-    err = moe::launch_layout(d_topk_idx, num_tokens, h->cfg.topk, h->cfg.num_experts,
-                             h->cfg.num_ranks, h->arrays, stream);
+    err = handle_layout(h, d_topk_idx, num_tokens, stream);
     if (err == hipSuccess)
-      err = moe::launch_dispatch(dtype, d_x, h->arrays.pos, d_out, d_scales, out_rows,
-                                 num_tokens, h->cfg.topk, h->cfg.hidden, h->max_workgroups,
-                                 stream);
+      err = handle_dispatch(h, dtype, d_x, d_out, d_scales, out_rows, num_tokens, stream);
   }
   if (err != hipSuccess) {
     h->ready = false;

@@ -82,6 +82,8 @@ struct LayoutOut {
   int32_t* rank_pos;       // rank pass: [T * R] row of each (token, rank), -1 if none
   int num_groups;          // R
   int per_rank;            // E / R
+  int2* order;             // expert pass, block_chunks > 0: rows of each dispatch block
+  int block_chunks;        // chunks per dispatch block; 0: no lists
 };
 
 __device__ __forceinline__ int rank_of(const Buckets& b, int e) {
@@ -158,19 +160,86 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(Buckets b, 
   for (int e = tid; e < b.nbuckets; e += kLayoutThreads) out[e] = s_hist[e];
 }
 
+// Exclusive scans of a[0 .. n) and, with kTwo, b[0 .. n) in LDS, in place
+// (n <= 2 * kLayoutThreads: two entries per thread), with a[n] and b[n] the
+// totals; both arrays go through the same shuffles and barriers. Every thread
+// of the workgroup calls it, after the arrays are complete; they and wsum
+// (2 * kLayoutWaves words) are free again on return.
+template <bool kTwo>
+__device__ __forceinline__ void workgroup_exclusive_scan(int32_t* a, int32_t* b, int n,
+                                                         int32_t* wsum) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i0 = 2 * tid, i1 = 2 * tid + 1;
+  const int a0 = i0 < n ? a[i0] : 0, a1 = i1 < n ? a[i1] : 0;
+  const int b0 = kTwo && i0 < n ? b[i0] : 0, b1 = kTwo && i1 < n ? b[i1] : 0;
+  const int la = a0 + a1, lb = b0 + b1;
+  int ia = la, ib = lb;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int ua = __shfl_up(ia, d, 64);
+    const int ub = kTwo ? __shfl_up(ib, d, 64) : 0;
+    if (lane >= d) {
+      ia += ua;
+      ib += ub;
+    }
+  }
+  if (lane == 63) {
+    wsum[wave] = ia;
+    if (kTwo) wsum[kLayoutWaves + wave] = ib;
+  }
+  __syncthreads();
+  int before_a = 0, total_a = 0, before_b = 0, total_b = 0;
+#pragma unroll
+  for (int w = 0; w < kLayoutWaves; ++w) {
+    const int wa = wsum[w];
+    before_a += w < wave ? wa : 0;
+    total_a += wa;
+    if (kTwo) {
+      const int wb = wsum[kLayoutWaves + w];
+      before_b += w < wave ? wb : 0;
+      total_b += wb;
+    }
+  }
+  const int ea = before_a + ia - la;
+  if (i0 < n) a[i0] = ea;
+  if (i1 < n) a[i1] = ea + a0;
+  if (tid == 0) a[n] = total_a;
+  if (kTwo) {
+    const int eb = before_b + ib - lb;
+    if (i0 < n) b[i0] = eb;
+    if (i1 < n) b[i1] = eb + b0;
+    if (tid == 0) b[n] = total_b;
+  }
+  __syncthreads();
+}
+
 // kSteps: 64-slot steps per wavefront. kSingle: one workgroup holds every
 // slot (up to kLayoutThreads * kSteps); no histogram kernel ran before it.
+//
+// Expert pass with o.block_chunks > 0 (several workgroups): the chunks are
+// grouped into dispatch blocks of block_chunks chunks, and the kernel also
+// lists each block's rows in ascending row order. Rows of bucket e that come
+// from block B form one run, starting after the rows earlier blocks put in e
+// (the column sum over earlier blocks' chunks), so a row's place in B's list
+// is the number of B's rows in buckets below e plus its rank in that run.
 template <bool kRanks, int kSteps, bool kSingle>
 __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b, LayoutOut o) {
   // s_cur[w * E + e]: wavefront w's running row cursor for bucket e.
   __shared__ int32_t s_cur[kLayoutWaves * MOE_EP_MAX_EXPERTS];
   __shared__ int32_t s_off[MOE_EP_MAX_EXPERTS + 1];
   __shared__ int32_t s_pre[MOE_EP_MAX_EXPERTS];
-  __shared__ int32_t s_wsum[kLayoutWaves];
+  __shared__ int32_t s_wsum[2 * kLayoutWaves];
+  // Dispatch lists: rows of each bucket in earlier blocks; then the block's
+  // own count per bucket, scanned.
+  __shared__ int32_t s_bpre[kRanks || kSingle ? 1 : MOE_EP_MAX_EXPERTS];
+  __shared__ int32_t s_bscan[kRanks || kSingle ? 1 : MOE_EP_MAX_EXPERTS + 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int E = b.nbuckets;
   const int nblocks = gridDim.x;
+  const bool lists = !kRanks && !kSingle && o.block_chunks > 0;
+  const int block_first = lists ? static_cast<int>(blockIdx.x) / o.block_chunks * o.block_chunks : 0;
+  const int block_end = lists ? min(block_first + o.block_chunks, nblocks) : 0;
 
   for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) s_cur[i] = 0;
   if (kRanks && kSingle) {   // every (token, rank) starts as "not routed there"
@@ -187,15 +256,21 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
   // Column sums of the per-workgroup histograms: the bucket totals, and the
   // part that earlier workgroups (earlier slots) contribute.
   for (int e = tid; e < E && !kSingle; e += kLayoutThreads) {
-    int tot = 0, pre = 0;
+    int tot = 0, pre = 0, bpre = 0, bown = 0;
 #pragma unroll 16
     for (int g = 0; g < nblocks; ++g) {
       const int v = o.hist[static_cast<size_t>(g) * E + e];
       tot += v;
       pre += g < static_cast<int>(blockIdx.x) ? v : 0;
+      bpre += g < block_first ? v : 0;
+      bown += g >= block_first && g < block_end ? v : 0;
     }
     s_off[e] = tot;
     s_pre[e] = pre;
+    if (!kRanks && !kSingle) {
+      s_bpre[e] = bpre;
+      s_bscan[e] = bown;
+    }
   }
   __syncthreads();
 
@@ -224,33 +299,23 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
     __syncthreads();
   }
 
-  // Exclusive scan of the totals over buckets (two entries per thread, <= 1024).
-  {
-    const int i0 = 2 * tid, i1 = 2 * tid + 1;
-    const int v0 = i0 < E ? s_off[i0] : 0;
-    const int v1 = i1 < E ? s_off[i1] : 0;
-    const int local = v0 + v1;
-    int incl = local;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int up = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += up;
+  // Exclusive scans over buckets: the totals (bucket offsets), and for the
+  // dispatch lists the block's own counts.
+  if (!kRanks && !kSingle && lists) {
+    workgroup_exclusive_scan<true>(s_off, s_bscan, E, s_wsum);
+    // A row p of bucket e lands at list place p - (s_off[e] + s_bpre[e]) +
+    // s_bscan[e]; keep that offset per bucket (in s_bpre).
+    for (int e = tid; e < E; e += kLayoutThreads) s_bpre[e] = s_bscan[e] - s_off[e] - s_bpre[e];
+    // The block's first workgroup marks the entries past its rows (invalid
+    // slots, the tail of a last block) as (-1, -1).
+    if (static_cast<int>(blockIdx.x) == block_first) {
+      const int bs = o.block_chunks * kLayoutChunk;
+      int2* list = o.order + static_cast<size_t>(block_first / o.block_chunks) * bs;
+      for (int i = s_bscan[E] + tid; i < bs; i += kLayoutThreads) list[i] = make_int2(-1, -1);
     }
-    if (lane == 63) s_wsum[wave] = incl;
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kLayoutWaves; ++w) {
-      const int ws = s_wsum[w];
-      before += w < wave ? ws : 0;
-      total += ws;
-    }
-    const int excl = before + incl - local;
-    if (i0 < E) s_off[i0] = excl;
-    if (i1 < E) s_off[i1] = excl + v0;
-    if (tid == 0) s_off[E] = total;
+  } else {
+    workgroup_exclusive_scan<false>(s_off, nullptr, E, s_wsum);
   }
-  __syncthreads();
 
   if (blockIdx.x == 0) {
     for (int e = tid; e < E; e += kLayoutThreads) {
@@ -311,6 +376,17 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
         const int t = slot / b.topk;
         o.src[p] = t;
         if (kRanks) o.rank_pos[static_cast<size_t>(t) * o.num_groups + e] = p;
+        if (!kRanks && !kSingle) {
+          if (lists) {
+            // Place in the block's list: its rows in lower buckets, then the
+            // rank of p in bucket e's run of this block.
+            const int bs = o.block_chunks * kLayoutChunk;
+            const int li = p + s_bpre[e];
+            if (li >= 0 && li < bs)
+              o.order[static_cast<size_t>(block_first / o.block_chunks) * bs + li] =
+                  make_int2(p, t);
+          }
+        }
       }
     }
   }
@@ -359,12 +435,16 @@ hipError_t launch_pass(const Buckets& b, const LayoutOut& o, hipStream_t stream)
 uint32_t rank_multiplier(int per) { return ((1u << 20) + per - 1) / per; }
 
 hipError_t launch_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,
-                         int num_ranks, const LayoutArrays& a, hipStream_t stream) {
+                         int num_ranks, const LayoutArrays& a, hipStream_t stream,
+                         int block_chunks) {
   const int per = num_experts / num_ranks;
   Buckets b{d_idx, num_tokens * topk, topk, num_experts, rank_multiplier(per),
             num_experts, bits_for(num_experts), num_tokens * topk};
+  // Lists only where several place workgroups run and the arrays exist.
+  const bool lists = block_chunks > 0 && b.slots > kLayoutSingleChunk && a.order != nullptr;
   LayoutOut o{a.hist, a.counts_e, a.offsets_e, a.counts_r, a.offsets_r, a.pos, a.src_idx,
-              a.status, nullptr, num_ranks, per};
+              a.status, nullptr, num_ranks, per, lists ? a.order : nullptr,
+              lists ? block_chunks : 0};
   return launch_pass<false>(b, o, stream);
 }
 

@@ -47,7 +47,69 @@ struct LayoutArrays {
   int32_t* hist;       // [layout_blocks(T_max * k)][E] per-workgroup histograms
   int32_t* pos;        // [T_max * k]
   int32_t* src_idx;    // [T_max * k]
+  // Row lists of the blocked bf16 dispatch (null when a caller has none):
+  // [dispatch_order_entries(T_max, k)] (row, token) pairs, block b's at b * bs,
+  // (-1, -1) past the block's rows.
+  int2* order;
 };
+
+// Blocked bf16 dispatch. The slots are cut into dispatch blocks of
+// block_chunks layout chunks (bs = block_chunks * kLayoutChunk slots); the
+// layout lists each block's rows in ascending row order, and the dispatch
+// gives block b to the workgroups of XCD slot b % kXcds, which walk the list:
+// every wavefront copies one 1 KiB slice of x[token] to out[row]. The rows a
+// block writes at once are then a run of consecutive rows per expert, and the
+// x rows of its tokens are read once from HBM (prefetched in token order) and
+// re-read from that XCD's L2.
+constexpr int kXcds = MOE_EP_XCDS;
+// x bytes a dispatch block's tokens should not exceed (one XCD's L2 is 4 MiB).
+constexpr int64_t kBlockXBytes = int64_t(4) << 20;
+
+// Layout chunks per dispatch block for num_tokens x topk slots of `hidden`
+// bf16 channels, or 0 when the blocked form is not used: fewer than one block
+// per XCD slot, or one chunk's tokens already hold more than kBlockXBytes of x.
+// A power of two (the dispatch finds a row's block with a shift), at most
+// kBlockXBytes of x and at most chunks / kXcds.
+inline int dispatch_block_chunks(int num_tokens, int topk, int hidden) {
+  const int64_t slots = int64_t(num_tokens) * topk;
+  const int64_t chunks = (slots + kLayoutChunk - 1) / kLayoutChunk;
+  if (topk <= 0 || hidden <= 0 || chunks < kXcds) return 0;
+  const int64_t chunk_x = int64_t(kLayoutChunk) * 2 * hidden / topk;
+  if (chunk_x > kBlockXBytes) return 0;
+  int64_t m = 1;
+  while (2 * m * chunk_x <= kBlockXBytes && 2 * m <= chunks / kXcds) m *= 2;
+  return static_cast<int>(m);
+}
+
+// Unsigned division by a divisor fixed at launch (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", 1994): with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, n / d equals
+// (mulhi(n, m) + n) >> l for every n < 2^31 (the sum then fits in 32 bits).
+// The kernels that use it do one multiply-high, one add and one shift per
+// division instead of a division routine.
+struct FastDiv {
+  uint32_t mul;
+  uint32_t shift;
+};
+
+inline FastDiv make_fast_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+  return FastDiv{static_cast<uint32_t>(m), l};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv d) {
+  return (__umulhi(n, d.mul) + n) >> d.shift;
+}
+
+// Entries of the order list for up to max_tokens x topk slots: every block
+// holds bs entries, and the last block of any batch ends at most
+// block_chunks - 1 <= chunks / kXcds chunks past the last slot.
+inline int64_t dispatch_order_entries(int max_tokens, int topk) {
+  const int64_t chunks = layout_blocks(int64_t(max_tokens) * topk);
+  return (chunks + chunks / kXcds + 1) * kLayoutChunk;
+}
 
 // Workspace regions of the rank-deduplicated layout.
 struct RankArrays {
@@ -73,8 +135,11 @@ hipError_t layout_scratch(int32_t** out);
 size_t layout_scratch_ints(int num_tokens, int topk, int num_experts);
 
 // Host-side launchers; each returns the hipError_t of its launches.
+// block_chunks > 0 also writes a.order for the blocked bf16 dispatch
+// (dispatch_block_chunks of the batch; needs more than 4096 slots).
 hipError_t launch_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,
-                         int num_ranks, const LayoutArrays& a, hipStream_t stream);
+                         int num_ranks, const LayoutArrays& a, hipStream_t stream,
+                         int block_chunks = 0);
 
 hipError_t launch_rank_layout(const int32_t* d_idx, int num_tokens, int topk, int num_experts,
                               int num_ranks, const RankArrays& a, hipStream_t stream);
@@ -85,6 +150,11 @@ hipError_t launch_rank_layout(const int32_t* d_idx, int num_tokens, int topk, in
 hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, void* d_out,
                            void* d_scales, int64_t rows, int num_tokens, int topk, int hidden,
                            int max_blocks, hipStream_t stream);
+
+// Blocked bf16 dispatch through the lists a layout with block_chunks wrote.
+hipError_t launch_dispatch_blocks(const void* d_x, const int2* d_order, void* d_out, int64_t rows,
+                                  int num_tokens, int topk, int hidden, int block_chunks,
+                                  hipStream_t stream);
 
 // bf16 dispatch for tables in which many slots are -1 (the rank-deduplicated
 // layout): one wavefront per (token, slice) loops over the slots, where

@@ -56,9 +56,11 @@ def test_workspace_bytes(lib):
     slots = 4096 * 8
     # expert layout: pos + src_idx + 32 histograms (one per 1024-slot workgroup) of 256
     # experts; rank layout: slot_row + rank_pos [T, 8] + src [T * 8] + 32 histograms of 8
-    # ranks; decode-time layout: pos [1024 * 8] + counts [256]; small arrays
+    # ranks; decode-time layout: pos [1024 * 8] + counts [256]; blocked bf16 dispatch: (row,
+    # token) lists of (32 + 32 / 8 + 1) blocks' worth of 1024 entries + 32 list lengths;
+    # small arrays
     need = (2 * 4 * slots + 32 * 256 * 4 + 4 * slots + 4 * 4096 * 8 + 4 * 4096 * 8 + 32 * 8 * 4
-            + 4 * 1024 * 8 + 4 * 256)
+            + 4 * 1024 * 8 + 4 * 256 + 8 * (32 + 4 + 1) * 1024 + 4 * 32)
     assert need <= n < need + 16 * 1024
     assert n % 256 == 0
     zero = lib.moe_workspace_bytes(ctypes.byref(cfg(0)))
