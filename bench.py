@@ -132,7 +132,7 @@ def queue_ahead():
         _QUEUE_AHEAD_BUF.fill_(i)
 
 
-KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_slots_kernel<2>",
+KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_blocks_kernel",
                 "dispatch_fp8": "dispatch_fp8_kernel", "combine": "combine_kernel<true>"}
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "traffic_deepseekv3.json")
@@ -369,6 +369,20 @@ def main():
                 "us_p10": round(float(np.percentile(us, 10)), 2),
                 "us_p90": round(float(np.percentile(us, 90)), 2)}
 
+
+    def per_slot_form(handle, fn, nbytes_op):
+        """The bf16 dispatch in its per-slot form (a workgroup cap above the item
+        count selects it, uncapped) and, right after it under the same
+        conditions, in the form the handle picks by default (blocked where that
+        applies): a same-box, back-to-back comparison."""
+        handle.set_max_workgroups(1 << 20)
+        try:
+            us = sustained_us(fn, args.sustained_iters)
+        finally:
+            handle.set_max_workgroups(0)
+        us_default = sustained_us(fn, args.sustained_iters)
+        return {"us_median": us, **rate(nbytes_op, us),
+                "default_form_us_median": us_default}
     def rate(nb, us):
         return {"GBps": round(nb / (us * 1e-6) / 1e9, 1),
                 "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -457,6 +471,11 @@ def main():
                 "positions_in_order": in_order,
                 "routing": "every slot of token t on expert t*k/(T*k/E), not the workload's"}
             h.layout(bufs["idx"][0])
+        # Context 5, same method and inputs: the bf16 dispatch in its per-slot
+        # form (a workgroup cap above the item count selects it, uncapped), for
+        # a same-box comparison with the blocked form the step uses.
+        context["dispatch_bf16_per_slot_form"] = per_slot_form(
+            h, lambda i: h.dispatch(B("xb", i), out=B("d_out", i)), nbytes["dispatch_bf16"])
 
     # Rank-deduplicated exchange (one row per (token, rank)), sustained method.
     exchange = {}
@@ -760,6 +779,8 @@ def main():
                 us = sustained_us(fn, args.sustained_iters)
                 warm[op] = {"us_median": us, **rate(nb[op], us)}
             row["x_cache_resident"] = warm
+            row["dispatch_bf16_per_slot_form"] = per_slot_form(ho, calls["dispatch_bf16"],
+                                                               nb["dispatch_bf16"])
             others[name] = row
             del ob_, ho
         torch.cuda.synchronize()

@@ -431,23 +431,39 @@ __global__ __launch_bounds__(64 * kSlotWaves) void dispatch_bf16_slots_kernel(
 // block, row by row in ascending order, the row's 1 KiB slices side by side.
 // A wavefront copies one slice of x[token] to out[row]. So one XCD writes a
 // run of consecutive rows per expert at a time instead of rows of all
-// experts at once, and reads its tokens' x through its own L2. Each of the
-// slot's first wavefront items also loads one x slice of the slot's tokens,
-// in token order, kBlockPrefetchItems items ahead of its own position: the
-// slot's x comes from HBM as one sequential read early in the kernel, and
-// the copies find it in L2 or the last-level cache. Measured at T=4096,
-// H=7168, top-8 of 256 (probes, x from HBM / x cached): the per-slot form
-// 100.2-101.0 / 91.6-92.7 us; this form 90.1-90.6 / 83.5-86.7 us with blocks
-// of 256 tokens and the prefetch 1024 items ahead (0 / 2048 / 4096 items:
-// 92.7 / 90.1-91.9 / 93.0-93.5 us from HBM); blocks of 128 tokens
-// 91.8-92.9, of 512 tokens (more x than L2 holds) 110-112; without the XCD
-// pinning 116-133. A wavefront moves only 1 KiB, so its scalar work bounds
-// the kernel: the same form with runtime divisions took 150 us, with a
-// separate list-length load and signed guards 100 us. Hence blocks of a
-// power of two chunks (a shift), one multiply-high division by the slice
-// count, lists padded with (-1, -1) instead of a length, unsigned guards;
-// two slices per wavefront, or one slice of 2-8 rows, measured 94-106 us.
-// Correctness never depends on where a workgroup runs.
+// experts at once, and reads its tokens' x through its own L2.
+//
+// Each of the slot's first wavefront items also loads one x slice of the
+// slot's tokens, in token order, kBlockPrefetchItems items ahead of its own
+// position, after its own
+// store (a load ahead of the store would hold the store back until it
+// returned): the slot's x then comes from HBM as one sequential burst early
+// in the kernel and the copies find it in L2 or the last-level cache, where
+// the copies alone would read each x row from HBM at the random moment its
+// first row comes up. Measured (probes, x from HBM / x cached, us):
+//   T=4096, H=7168, top-8 of 256: per-slot form 98.4-100.7 / 90.1-93.2;
+//     blocks of 2 chunks (3.5 MB of x) 94.8-96.9 / 76.9-77.4 without the
+//     prefetch, 91.6 / 85.3 with it (issued before the store: 92.2 / 95.0);
+//     blocks of 1 chunk 91.1-92.8 / 87.7-92.2 with it; blocks of 4 chunks
+//     (7 MB, more x than an L2 holds) 111; without the XCD pinning 116-133.
+//   T=4096, H=2048, top-6 of 64: per-slot form 22.7-22.8 / 18.5-19.0; blocks
+//     of 1 chunk 21.8 / 17.2 with the prefetch, 23.1-23.2 / 17.7 without;
+//     blocks of 2 chunks (12 blocks over 8 slots) 24.2-28.0.
+//   T=16384, H=4096, top-8 of 128, 98% of tokens on expert 0 (16.8 MB of x
+//     per slot): per-slot form 223-225 / 200-201; blocks of 2 or 4 chunks
+//     203.8-205.2 / 174.4-186.5 without the prefetch, 211.7-277.7 with it
+//     (the burst evicts the blocks' own x from L2); with the workload's
+//     Zipf routing the blocked form lost (209.2 against 204.1), so slots
+//     holding more than kPrefetchSlotXBytes of x keep the per-slot form. A
+//     prefetch spread evenly over the kernel, one block ahead, was slower at
+//     every shape (112-301).
+// A wavefront moves only 1 KiB, so its scalar work bounds the kernel: the
+// same form with runtime divisions took 150 us, with a separate list-length
+// load and signed guards 100 us. Hence blocks of a power of two chunks (a
+// shift), one multiply-high division by the slice count, lists padded with
+// (-1, -1) instead of a length, unsigned guards; two slices per wavefront,
+// or one slice of 2-8 rows, measured 94-106 us. Correctness never depends
+// on where a workgroup runs.
 constexpr int kBlockPrefetchItems = 1024;
 
 __global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_blocks_kernel(
@@ -462,10 +478,16 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_blocks_kernel(
   const int b = slot + kXcds * (ri_all >> bs_log2);
   if (b >= nblocks) return;
   const int2 rt = order[(static_cast<size_t>(b) << bs_log2) + (ri_all & ((1 << bs_log2) - 1))];
+  // The copy: one unconditional load (clamped), one guarded store.
+  const bool ok = static_cast<uint32_t>(rt.x) < rows && static_cast<uint32_t>(rt.y) < num_tokens;
+  const int v = sl * 64 + lane;
+  const int vc = v < nvec ? v : nvec - 1;
+  const u32x4 r = x[static_cast<size_t>(ok ? rt.y : 0) * nvec + vc];
+  loaded(r);
+  if (ok && v < nvec) store_row(&out[static_cast<size_t>(rt.x) * nvec + v], r);
   // Prefetch: position li + ahead of the slot's token-order sequence of x
   // slices, tpb token positions per block (a block's slots [b*bs, (b+1)*bs)
   // span at most bs/k + 2 tokens; positions past its last token re-read it).
-  u32x4 pf = {0u, 0u, 0u, 0u};
   const uint32_t pi = static_cast<uint32_t>(li) + kBlockPrefetchItems;
   if (pi < prefetch_items) {
     const int lt_all = fast_div(pi, div_slices);
@@ -482,17 +504,10 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_blocks_kernel(
       tok = tok < last ? tok : last;
       int pv = psl * 64 + lane;
       pv = pv < nvec ? pv : nvec - 1;
-      pf = x[static_cast<size_t>(tok) * nvec + pv];
+      const u32x4 pf = x[static_cast<size_t>(tok) * nvec + pv];
+      asm volatile("" ::"v"(pf));
     }
   }
-  // The copy: one unconditional load (clamped), one guarded store.
-  const bool ok = static_cast<uint32_t>(rt.x) < rows && static_cast<uint32_t>(rt.y) < num_tokens;
-  const int v = sl * 64 + lane;
-  const int vc = v < nvec ? v : nvec - 1;
-  const u32x4 r = x[static_cast<size_t>(ok ? rt.y : 0) * nvec + vc];
-  loaded(r);
-  if (ok && v < nvec) store_row(&out[static_cast<size_t>(rt.x) * nvec + v], r);
-  asm volatile("" ::"v"(pf));
 }
 
 // FP8 and MXFP8 dispatch: each wavefront also loads the x slice of the item

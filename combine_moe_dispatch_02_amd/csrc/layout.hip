@@ -233,6 +233,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
   // own count per bucket, scanned.
   __shared__ int32_t s_bpre[kRanks || kSingle ? 1 : MOE_EP_MAX_EXPERTS];
   __shared__ int32_t s_bscan[kRanks || kSingle ? 1 : MOE_EP_MAX_EXPERTS + 1];
+  // Partial column sums when several threads share a bucket.
+  __shared__ int32_t s_part[kSingle ? 1 : 4][kSingle ? 1 : kLayoutThreads];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int E = b.nbuckets;
@@ -253,23 +255,66 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
   int ids[kSteps];
   load_buckets<kRanks, kSteps>(b, base, lane, ids);
 
-  // Column sums of the per-workgroup histograms: the bucket totals, and the
-  // part that earlier workgroups (earlier slots) contribute.
-  for (int e = tid; e < E && !kSingle; e += kLayoutThreads) {
-    int tot = 0, pre = 0, bpre = 0, bown = 0;
+  // Column sums of the per-workgroup histograms: the bucket totals, the part
+  // that earlier workgroups (earlier slots) contribute and, for the dispatch
+  // lists, the parts of earlier blocks and of this workgroup's own block.
+  // With fewer buckets than threads, `parts` threads share a bucket, each
+  // summing a contiguous range of the histograms, and LDS adds the ranges up
+  // (the sums are latency-bound: each thread's loads come back in batches of
+  // 16, so fewer loads per thread is less time).
+  if (!kSingle) {
+    int parts = 1;
+    while (parts * 2 * E <= kLayoutThreads && parts < kLayoutWaves) parts *= 2;
+    const int me = static_cast<int>(blockIdx.x);
+    for (int i = tid; i < E * parts; i += kLayoutThreads) {
+      const int e = i % E, part = i / E;
+      const int g0 = part * nblocks / parts, g1 = (part + 1) * nblocks / parts;
+      int tot = 0, pre = 0, bpre = 0, bown = 0;
 #pragma unroll 16
-    for (int g = 0; g < nblocks; ++g) {
-      const int v = o.hist[static_cast<size_t>(g) * E + e];
-      tot += v;
-      pre += g < static_cast<int>(blockIdx.x) ? v : 0;
-      bpre += g < block_first ? v : 0;
-      bown += g >= block_first && g < block_end ? v : 0;
+      for (int g = g0; g < g1; ++g) {
+        const int v = o.hist[static_cast<size_t>(g) * E + e];
+        tot += v;
+        pre += g < me ? v : 0;
+        if (!kRanks) {
+          bpre += g < block_first ? v : 0;
+          bown += g >= block_first && g < block_end ? v : 0;
+        }
+      }
+      if (parts == 1) {
+        s_off[e] = tot;
+        s_pre[e] = pre;
+        if (!kRanks) {
+          s_bpre[e] = bpre;
+          s_bscan[e] = bown;
+        }
+      } else {
+        s_part[0][i] = tot;
+        s_part[1][i] = pre;
+        if (!kRanks) {
+          s_part[2][i] = bpre;
+          s_part[3][i] = bown;
+        }
+      }
     }
-    s_off[e] = tot;
-    s_pre[e] = pre;
-    if (!kRanks && !kSingle) {
-      s_bpre[e] = bpre;
-      s_bscan[e] = bown;
+    if (parts > 1) {
+      __syncthreads();
+      for (int e = tid; e < E; e += kLayoutThreads) {
+        int tot = 0, pre = 0, bpre = 0, bown = 0;
+        for (int q = 0; q < parts; ++q) {
+          tot += s_part[0][q * E + e];
+          pre += s_part[1][q * E + e];
+          if (!kRanks) {
+            bpre += s_part[2][q * E + e];
+            bown += s_part[3][q * E + e];
+          }
+        }
+        s_off[e] = tot;
+        s_pre[e] = pre;
+        if (!kRanks) {
+          s_bpre[e] = bpre;
+          s_bscan[e] = bown;
+        }
+      }
     }
   }
   __syncthreads();
