@@ -419,8 +419,10 @@ def main():
             warm[name] = {"us_median": us, **rate(nbytes[name], us)}
         context["x_cache_resident"] = warm
         # Context 2: a cross-check of the cold-input method -- every timed call
-        # follows a 1 GiB read sweep (a reduction; no dirty lines), outside its
-        # events.
+        # follows a 1 GiB read sweep (a reduction; no dirty lines) and then the
+        # layout of the same ids (as in a step, where the layout's outputs are
+        # fresh when the dispatch reads them; the sweep alone would evict them
+        # too), both outside its events.
         sweep_src = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
         sink = torch.zeros((), dtype=torch.float32, device=dev)
         evicted = {}
@@ -428,6 +430,7 @@ def main():
             evs = [(HipTimer(), HipTimer()) for _ in range(args.sustained_iters)]
             for i in range(3 + args.sustained_iters):
                 sink.copy_(sweep_src.amax())
+                h.layout(bufs["idx"][0])
                 if i >= 3:
                     evs[i - 3][0].record(stream)
                 run_op(name, i)
