@@ -134,7 +134,11 @@ void moe_handle_destroy(moe_handle_t h);
  * d_topk_idx: int32 [num_tokens, topk] row-major, 0 <= num_tokens <= max_tokens.
  * Writes pos, src_idx, counts, offsets and status into the workspace on
  * `stream`; no host synchronisation. Marks the handle ready for dispatch and
- * combine with this num_tokens. */
+ * combine with this num_tokens. For batches of at least 8 x 1024 slots where
+ * each of the 8 XCDs' share of x is at most 8 MiB, it also writes, per block
+ * of consecutive slots, the block's rows in ascending order (row, token), which
+ * the bf16 dispatch then copies block by block, one XCD per block: the same
+ * rows, written one run per expert at a time. */
 int moe_dispatch_layout(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_tokens,
                         hipStream_t stream);
 
@@ -179,7 +183,10 @@ int moe_dispatch_layout_noalloc(const int32_t* d_topk_idx, int32_t num_tokens, i
  *                         amax) - 8 clamped to [-127, 127], elements E4M3
  *                         nearest-even of x / 2^shared clamped to +-448;
  *                         an all-zero block has code 0).
- * Row pos[t*k+j] receives token t; rows past the valid total are not written. */
+ * Row pos[t*k+j] receives token t; rows past the valid total are not written.
+ * The bf16 rows are bit-identical whichever kernel form the layout selected
+ * (the per-XCD block form above, or one workgroup per token slice; a workgroup
+ * cap, moe_set_max_workgroups, always selects the latter). */
 int moe_dispatch(moe_handle_t h, const void* d_x, int dtype, void* d_out, void* d_scales,
                  int64_t out_rows, hipStream_t stream);
 
