@@ -177,12 +177,13 @@ int hip_status(hipError_t err, const char* fn) {
 // dispatch wherever that form applies to the batch.
 hipError_t handle_layout(moe_handle_t h, const int32_t* d_idx, int32_t num_tokens,
                          hipStream_t stream) {
-  int chunks = moe::dispatch_block_chunks(num_tokens, h->cfg.topk, h->cfg.hidden);
-  if (int64_t(num_tokens) * h->cfg.topk <= moe::kLayoutSingleChunk) chunks = 0;
+  // (dispatch_block_chunks is 0 below 8 chunks, so the lists never meet the
+  // one-workgroup layout, which writes none.)
+  const int block_chunks = moe::dispatch_block_chunks(num_tokens, h->cfg.topk, h->cfg.hidden);
   h->order_chunks = 0;
   const hipError_t err = moe::launch_layout(d_idx, num_tokens, h->cfg.topk, h->cfg.num_experts,
-                                            h->cfg.num_ranks, h->arrays, stream, chunks);
-  if (err == hipSuccess) h->order_chunks = chunks;
+                                            h->cfg.num_ranks, h->arrays, stream, block_chunks);
+  if (err == hipSuccess) h->order_chunks = block_chunks;
   return err;
 }
 

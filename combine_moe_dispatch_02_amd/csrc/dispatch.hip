@@ -435,12 +435,12 @@ __global__ __launch_bounds__(64 * kSlotWaves) void dispatch_bf16_slots_kernel(
 //
 // Each of the slot's first wavefront items also loads one x slice of the
 // slot's tokens, in token order, kBlockPrefetchItems items ahead of its own
-// position, after its own
-// store (a load ahead of the store would hold the store back until it
-// returned): the slot's x then comes from HBM as one sequential burst early
-// in the kernel and the copies find it in L2 or the last-level cache, where
-// the copies alone would read each x row from HBM at the random moment its
-// first row comes up. Measured (probes, x from HBM / x cached, us):
+// position, after its own store (vector loads retire in order, so a load
+// ahead of the store would hold the store back until it returned): the
+// slot's x then comes from HBM as one sequential burst early in the kernel
+// and the copies find it in L2 or the last-level cache, where the copies
+// alone would read each x row from HBM at the random moment its first row
+// comes up. Measured (probes, x from HBM / x cached, us):
 //   T=4096, H=7168, top-8 of 256: per-slot form 98.4-100.7 / 90.1-93.2;
 //     blocks of 2 chunks (3.5 MB of x) 94.8-96.9 / 76.9-77.4 without the
 //     prefetch, 91.6 / 85.3 with it (issued before the store: 92.2 / 95.0);
@@ -458,8 +458,8 @@ __global__ __launch_bounds__(64 * kSlotWaves) void dispatch_bf16_slots_kernel(
 //     prefetch spread evenly over the kernel, one block ahead, was slower at
 //     every shape (112-301).
 // A wavefront moves only 1 KiB, so its scalar work bounds the kernel: the
-// same form with runtime divisions took 150 us, with a separate list-length
-// load and signed guards 100 us. Hence blocks of a power of two chunks (a
+// same form with runtime divisions took 139-153 us, with a separate
+// list-length load and signed guards 100 us. Hence blocks of a power of two chunks (a
 // shift), one multiply-high division by the slice count, lists padded with
 // (-1, -1) instead of a length, unsigned guards; two slices per wavefront,
 // or one slice of 2-8 rows, measured 94-106 us. Correctness never depends
