@@ -138,18 +138,26 @@ TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profile
                             "traffic_deepseekv3.json")
 
 
+def sources_sha256(paths) -> str:
+    """SHA-256 over the named files' bytes, in order (paths from the repository root)."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(root, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(op: str):
     """HBM bytes per launch of op's kernel from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the kernel's
-    source has changed since the counters were taken."""
-    import hashlib
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when any source the
+    kernel is compiled from has changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)["kernels"][KERNEL_OF_OP[op]]
-        root = os.path.dirname(os.path.abspath(__file__))
-        with open(os.path.join(root, rec["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
-                return None
+        if sources_sha256(rec["sources"]) != rec["sources_sha256"]:
+            return None
         return int(rec["traffic_bytes"])
     except (OSError, KeyError, ValueError):
         return None
@@ -816,9 +824,9 @@ def main():
                      "traffic_source": (f"{os.path.relpath(TRAFFIC_FILE, os.path.dirname(os.path.abspath(__file__)))}"
                                         f" [{KERNEL_OF_OP[dominant]}]: rocprofv3 FETCH_SIZE + "
                                         "WRITE_SIZE per launch, copy-calibrated, taken from "
-                                        "the same kernel source (hash-checked)")
+                                        "the same kernel sources (hash-checked)")
                      if traffic is not None else
-                     "none: the kernel's source changed since the counters were taken"},
+                     "none: a source of the kernel changed since the counters were taken"},
         "ops": per_op,
         "instrumented_steps": len(instrumented),
         "sustained": sustained,

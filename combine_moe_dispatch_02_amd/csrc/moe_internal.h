@@ -123,8 +123,9 @@ inline FastDiv make_fast_div(uint32_t d) {
   return FastDiv{static_cast<uint32_t>(m), l};
 }
 
-__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv d) {
-  return (__umulhi(n, d.mul) + n) >> d.shift;
+__host__ __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv d) {
+  const uint32_t hi = static_cast<uint32_t>((static_cast<uint64_t>(n) * d.mul) >> 32);
+  return (hi + n) >> d.shift;
 }
 
 // Entries of the order list for up to max_tokens x topk slots: every block
