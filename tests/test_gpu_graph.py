@@ -65,8 +65,12 @@ def test_decode_step_graph_replays():
             assert np.array_equal(host_bits(got[2]), np.where(xb == 0x8000, np.uint16(0), xb))
 
 
-def test_standard_step_graph_replays():
-    T, H, k, E, R = 512, 2048, 6, 64, 8
+@pytest.mark.parametrize("T", [512, 2048])
+def test_standard_step_graph_replays(T):
+    """512 tokens: the one-workgroup layout and the per-slot bf16 dispatch;
+    2048 tokens (12 layout chunks): the two layout kernels with the block
+    lists and the blocked bf16 dispatch."""
+    H, k, E, R = 2048, 6, 64, 8
     h = Handle(T, H, k, E, R)
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
@@ -112,5 +116,6 @@ def test_standard_step_graph_replays():
         if seed == 5:
             lay = oracle.layout(ri, E, R)
             assert np.array_equal(got[0].cpu().numpy(), lay["pos"])
+            assert np.array_equal(host_bits(got[1]), oracle.dispatch_bf16(xb, lay["pos"]))
             want, mag = oracle.combine(yb, rw, lay["pos"], return_magnitude=True)
             assert_combine_close(host_bits(got[4]), want, mag, k)
