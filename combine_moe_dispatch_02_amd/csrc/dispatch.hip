@@ -449,14 +449,17 @@ __global__ __launch_bounds__(64 * kSlotWaves) void dispatch_bf16_slots_kernel(
 //   T=4096, H=2048, top-6 of 64: per-slot form 22.7-22.8 / 18.5-19.0; blocks
 //     of 1 chunk 21.8 / 17.2 with the prefetch, 23.1-23.2 / 17.7 without;
 //     blocks of 2 chunks (12 blocks over 8 slots) 24.2-28.0.
-//   T=16384, H=4096, top-8 of 128, 98% of tokens on expert 0 (16.8 MB of x
-//     per slot): per-slot form 223-225 / 200-201; blocks of 2 or 4 chunks
-//     203.8-205.2 / 174.4-186.5 without the prefetch, 211.7-277.7 with it
-//     (the burst evicts the blocks' own x from L2); with the workload's
-//     Zipf routing the blocked form lost (209.2 against 204.1), so slots
-//     holding more than kPrefetchSlotXBytes of x keep the per-slot form. A
-//     prefetch spread evenly over the kernel, one block ahead, was slower at
-//     every shape (112-301).
+//   T=16384, H=4096, top-8 of 128 (16.8 MB of x per slot, more than an L2
+//     holds; the burst then lands in the last-level cache), x from HBM
+//     only, one box: per-slot form 218.7, blocks of 2 chunks 197.6 with the
+//     prefetch, 207.0 without; with Zipf routing per-slot 203.4, blocks of 2
+//     chunks 191-198 with it, 190.2 without, of 4 chunks (4 MB) 203-210.
+//     T=8192, H=7168: per-slot 203.6, blocked 185.8 with it, 194.0 without.
+//     T=16384, H=2048, top-6 of 64: per-slot 80.6, blocked 77.4 with it,
+//     82.7 without. A prefetch spread evenly over the kernel, one block ahead,
+//     was slower at every shape (112-301), and so was one where each
+//     block's last items fetched the next block (88-95 at T=4096, H=7168,
+//     225-246 with Zipf routing).
 // A wavefront moves only 1 KiB, so its scalar work bounds the kernel: the
 // same form with runtime divisions took 139-153 us, with a separate
 // list-length load and signed guards 100 us. Hence blocks of a power of two chunks (a

@@ -62,27 +62,21 @@ struct LayoutArrays {
 // x rows of its tokens are read once from HBM (prefetched in token order) and
 // re-read from that XCD's L2.
 constexpr int kXcds = MOE_EP_XCDS;
-// x bytes a dispatch block's tokens should not exceed (one XCD's L2 is 4 MiB).
-constexpr int64_t kBlockXBytes = int64_t(4) << 20;
-
-// The blocked dispatch reads an XCD slot's x as one prefetched burst; it is
-// used only while a slot's tokens hold at most this much x. Measured with the
-// workloads' routing, same box (x from HBM, us, blocked / per-slot form):
-// T=4096, H=7168, top-8 of 256 (7.4 MB per slot) 90.4 / 100.0; T=4096,
-// H=2048, top-6 of 64 (2.1 MB) 22.0 / 23.2; T=16384, H=4096, top-8 of 128,
-// Zipf-skewed (16.8 MB per slot, where the burst would evict the blocks' own
-// x from L2, so the blocked form ran without it) 209.2 / 204.1.
-constexpr int64_t kPrefetchSlotXBytes = int64_t(8) << 20;
+// x bytes a dispatch block's tokens may hold: 7/8 of one XCD's 4 MiB L2, so
+// that the tail of one block and the head of the next still fit it. Blocks
+// of the full 4 MiB were slower wherever a slot walked several of them
+// (same box, x from HBM, us, blocks of 4 MiB / 2 MiB: T=16384, H=4096,
+// top-8 of 128, Zipf routing 203.4 / 194; T=4096, H=4096, 51.8 / 47.8).
+constexpr int64_t kBlockXBytes = int64_t(7) << 19;
 
 // Layout chunks per dispatch block for num_tokens x topk slots of `hidden`
 // bf16 channels, or 0 when the blocked form is not used: fewer than one block
-// per XCD slot, one chunk's tokens already holding more than kBlockXBytes of
-// x, or a slot's tokens more than kPrefetchSlotXBytes. A power of two (the
-// dispatch finds a row's block with a shift) with at most kBlockXBytes of x
-// and at most chunks / kXcds chunks, chosen so that the busiest XCD slot gets
-// as few chunks as possible (blocks b, b + 8, ... share a slot: with 24
-// chunks, blocks of 2 would give four slots 4 chunks and four slots 2), the
-// larger block on a tie.
+// per XCD slot, or one chunk's tokens already holding more than kBlockXBytes
+// of x. A power of two (the dispatch finds a row's block with a shift) with
+// at most kBlockXBytes of x and at most chunks / kXcds chunks, chosen so that
+// the busiest XCD slot gets as few chunks as possible (blocks b, b + 8, ...
+// share a slot: with 24 chunks, blocks of 2 would give four slots 4 chunks
+// and four slots 2), the larger block on a tie.
 inline int dispatch_block_chunks(int num_tokens, int topk, int hidden) {
   const int64_t slots = int64_t(num_tokens) * topk;
   const int64_t chunks = (slots + kLayoutChunk - 1) / kLayoutChunk;
@@ -98,10 +92,6 @@ inline int dispatch_block_chunks(int num_tokens, int topk, int hidden) {
       best_load = load;
     }
   }
-  // x of one slot's token positions: per slot, bs / topk + 2 tokens per block.
-  const int64_t bs = best * kLayoutChunk;
-  const int64_t per_slot = ((chunks + best - 1) / best + kXcds - 1) / kXcds;
-  if (per_slot * (bs / topk + 2) * 2 * hidden > kPrefetchSlotXBytes) return 0;
   return static_cast<int>(best);
 }
 

@@ -134,11 +134,12 @@ void moe_handle_destroy(moe_handle_t h);
  * d_topk_idx: int32 [num_tokens, topk] row-major, 0 <= num_tokens <= max_tokens.
  * Writes pos, src_idx, counts, offsets and status into the workspace on
  * `stream`; no host synchronisation. Marks the handle ready for dispatch and
- * combine with this num_tokens. For batches of at least 8 x 1024 slots where
- * each of the 8 XCDs' share of x is at most 8 MiB, it also writes, per block
- * of consecutive slots, the block's rows in ascending order (row, token), which
- * the bf16 dispatch then copies block by block, one XCD per block: the same
- * rows, written one run per expert at a time. */
+ * combine with this num_tokens. For batches of at least 8 x 1024 slots whose
+ * 1024-slot chunks each cover at most 3.5 MiB of x (1024 / topk tokens of
+ * 2 * hidden bytes), it also writes, per block of consecutive slots, the
+ * block's rows in ascending order (row, token), which the bf16 dispatch then
+ * copies block by block, one XCD per block: the same rows, written one run per
+ * expert at a time. */
 int moe_dispatch_layout(moe_handle_t h, const int32_t* d_topk_idx, int32_t num_tokens,
                         hipStream_t stream);
 

@@ -60,7 +60,6 @@ void check_block_rule() {
         const int64_t nblocks = (chunks + m - 1) / m;
         const int64_t per_slot = (nblocks + moe::kXcds - 1) / moe::kXcds;
         const int64_t tpb = bs / k + 2;
-        if (per_slot * tpb * 2 * hidden > moe::kPrefetchSlotXBytes) fail("slot x above the limit", T, k, m);
         // the lists of this batch fit the workspace of any T_max >= T
         if (nblocks * bs > moe::dispatch_order_entries(T, k)) fail("lists above capacity", T, k, m);
         // every block's slots span at most tpb tokens
@@ -76,7 +75,13 @@ void check_block_rule() {
   // the shapes the benchmark measures
   if (moe::dispatch_block_chunks(4096, 8, 7168) != 2) fail("V3-like rule", 4096, 8, 7168);
   if (moe::dispatch_block_chunks(4096, 6, 2048) != 1) fail("16B-like rule", 4096, 6, 2048);
-  if (moe::dispatch_block_chunks(16384, 8, 4096) != 0) fail("Qwen3-like rule", 16384, 8, 4096);
+  if (moe::dispatch_block_chunks(16384, 8, 4096) != 2) fail("Qwen3-like rule", 16384, 8, 4096);
+  if (moe::dispatch_block_chunks(4096, 8, 4096) != 2) fail("H=4096 rule", 4096, 8, 4096);
+  if (moe::dispatch_block_chunks(16384, 6, 2048) != 4) fail("16B-like rule, long batch", 16384, 6, 2048);
+  // one chunk's tokens above 7/8 of an L2: the per-slot form
+  if (moe::dispatch_block_chunks(65536, 2, 7168) != 0) fail("top-2 at H=7168", 65536, 2, 7168);
+  if (moe::dispatch_block_chunks(896, 8, 7168) != 0) fail("under 8 chunks", 896, 8, 7168);
+  if (moe::dispatch_block_chunks(897, 8, 7168) != 1) fail("8 chunks", 897, 8, 7168);
 }
 
 }  // namespace

@@ -1,7 +1,7 @@
 """bf16 dispatch in its blocked form against the oracle and the per-slot form.
 
 From eight layout chunks of slots on (and while one chunk's tokens hold at
-most 4 MiB of x), the layout also lists, for each dispatch block of whole
+most 3.5 MiB of x), the layout also lists, for each dispatch block of whole
 chunks, the block's rows in ascending row order, and the bf16 dispatch copies
 x along those lists, one XCD slot per block. The rows must be bit-identical
 to the oracle's ("Inside the Nebius + PyTorch DeepSeek V3 recipe", section
@@ -10,8 +10,10 @@ experts its router picked) and to the per-slot form, which a workgroup cap
 selects; rows past the placed total stay untouched. Cases: exactly eight
 chunks and one more, blocks whose edges split a token's slots, a row whose
 last slice holds one 16-byte vector, the narrowest row, every slot on one
-expert, invalid ids, k = 1 and k = 32, a handle reused across sizes that take
-different forms, and the one-call layout + dispatch.
+expert, invalid ids, k = 1 and k = 32, XCD slots that walk two and eight
+blocks, 128 layout workgroups (column sums split over threads) feeding blocks
+of 16 chunks, a handle reused across sizes that take different forms, and the
+one-call layout + dispatch.
 """
 import numpy as np
 import pytest
@@ -60,6 +62,12 @@ CASES = [
     ("one_expert", 4096, 8, 256, 8, 1024, "const"),
     ("k32_invalid", 600, 32, 1024, 8, 1024, "invalid"),
     ("k1", 9000, 1, 64, 8, 512, "random"),
+    # 32 chunks of 912 KiB of x: blocks of 2 chunks, two per XCD slot
+    ("two_blocks_per_slot", 32768, 1, 64, 8, 456, "random"),
+    # 64 chunks of 2 MiB: blocks of 1 chunk, eight per slot; last slice one vector
+    ("eight_blocks_per_slot", 65536, 1, 64, 8, 1032, "random"),
+    # 128 chunks of 16 KiB: blocks of 16 chunks, the layout's split column sums
+    ("split_sums_lists", 16384, 8, 128, 8, 64, "invalid"),
 ]
 
 
