@@ -642,7 +642,7 @@ constexpr int kFixedSharedFrom = 256;   // tokens from which a workgroup shares 
 //     slot's row is e*C + r, r = earlier slots with its id, dropped from C on;
 //   packed (kPacked = true): the standard layout -- a slot's row is the number
 //     of valid slots with a smaller id plus r, so expert e's rows start at
-//     offsets_e[e] -- exactly what the two layout kernels produce.
+//     offsets_e[e] -- exactly what the layout kernels produce.
 template <bool kPacked>
 struct FusedLayout {
   const int32_t* idx;   // [T, k] expert ids

@@ -22,7 +22,8 @@
 // Up to 4096 slots (512 tokens at top-8) one workgroup of the place kernel
 // does both, each wavefront taking 128, 256 or 512 slots (as few as cover
 // them): its own per-wavefront counts are the totals. Beyond that,
-// workgroups of 1024 slots.
+// workgroups of 1024 slots; for the expert pass up to kLayoutFusedBlocks of
+// them, the place kernel alone, each workgroup counting every slot itself.
 //
 // Inside a wavefront, lanes that hold the same expert id find each other with
 // ceil(log2 E) ballots (one per id bit); the lowest lane of each group does
@@ -215,6 +216,8 @@ __device__ __forceinline__ void workgroup_exclusive_scan(int32_t* a, int32_t* b,
 
 // kSteps: 64-slot steps per wavefront. kSingle: one workgroup holds every
 // slot (up to kLayoutThreads * kSteps); no histogram kernel ran before it.
+// kFused (expert pass, several workgroups, up to kLayoutFusedBlocks): no
+// histogram kernel either; every workgroup counts all slots itself.
 //
 // Expert pass with o.block_chunks > 0 (several workgroups): the chunks are
 // grouped into dispatch blocks of block_chunks chunks, and the kernel also
@@ -222,9 +225,10 @@ __device__ __forceinline__ void workgroup_exclusive_scan(int32_t* a, int32_t* b,
 // from block B form one run, starting after the rows earlier blocks put in e
 // (the column sum over earlier blocks' chunks), so a row's place in B's list
 // is the number of B's rows in buckets below e plus its rank in that run.
-template <bool kRanks, int kSteps, bool kSingle, bool kLists>
+template <bool kRanks, int kSteps, bool kSingle, bool kLists, bool kFused = false>
 __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b, LayoutOut o) {
   static_assert(!kLists || (!kRanks && !kSingle), "lists: expert pass, several workgroups");
+  static_assert(!kFused || (!kRanks && !kSingle), "fused: expert pass, several workgroups");
   // s_cur[w * E + e]: wavefront w's running row cursor for bucket e.
   __shared__ int32_t s_cur[kLayoutWaves * MOE_EP_MAX_EXPERTS];
   __shared__ int32_t s_off[MOE_EP_MAX_EXPERTS + 1];
@@ -235,7 +239,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
   __shared__ int32_t s_bpre[kLists ? MOE_EP_MAX_EXPERTS : 1];
   __shared__ int32_t s_bscan[kLists ? MOE_EP_MAX_EXPERTS + 1 : 1];
   // Partial column sums when several threads share a bucket.
-  __shared__ int32_t s_part[kSingle ? 1 : 2][kSingle ? 1 : kLayoutThreads];
+  __shared__ int32_t s_part[kSingle || kFused ? 1 : 2][kSingle || kFused ? 1 : kLayoutThreads];
+  // Fused: counts per bucket of four ranges of chunks (see below).
+  __shared__ int32_t s_range[kFused ? 4 * MOE_EP_MAX_EXPERTS : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int E = b.nbuckets;
@@ -244,6 +250,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
   const int block_end = kLists ? min(block_first + o.block_chunks, nblocks) : 0;
 
   for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) s_cur[i] = 0;
+  if constexpr (kFused)
+    for (int i = tid; i < 4 * E; i += kLayoutThreads) s_range[i] = 0;
   if (kRanks && kSingle) {   // every (token, rank) starts as "not routed there"
     const int cells = (b.slots / b.topk) * o.num_groups;
     for (int i = tid; i < cells; i += kLayoutThreads) o.rank_pos[i] = -1;
@@ -264,7 +272,48 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(Buckets b,
   // 16, so fewer loads per thread is less time; it pays from 64 workgroups:
   // layout 14.3 -> 11.7 us at 131,072 slots over 128 experts, nothing
   // measurable at 32 workgroups).
-  if (!kSingle) {
+  if constexpr (kFused) {
+    // Every workgroup counts every slot, by plain LDS atomics (a count needs
+    // no per-lane rank, so no ballot grouping), into one of four ranges of
+    // chunks: before this workgroup's dispatch block, the block's chunks
+    // before this one, this one and the block's later chunks, and the chunks
+    // after the block (without lists the block is this chunk alone). The
+    // ids are read from L2 after the first workgroup of an XCD brings them
+    // in, sixteen 64-slot steps per wavefront in flight at a time. The range
+    // is uniform over a step (16 steps to a chunk).
+    __syncthreads();   // s_range cleared
+    const int me = static_cast<int>(blockIdx.x);
+    const int lo = kLists ? block_first : me, hi = kLists ? block_end : me;
+    constexpr int kStepsPerChunk = kLayoutChunk / 64;
+    constexpr int kBatch = 16;
+    const int steps = (b.slots + 63) / 64;
+    for (int st0 = wave; st0 < steps; st0 += kBatch * kLayoutWaves) {
+      int v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int slot = (st0 + u * kLayoutWaves) * 64 + lane;
+        v[u] = slot < b.slots ? b.idx[slot] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int c = (st0 + u * kLayoutWaves) / kStepsPerChunk;
+        const int r = c < lo ? 0 : c < me ? 1 : c < hi ? 2 : 3;
+        if (static_cast<unsigned>(v[u]) < static_cast<unsigned>(b.num_experts))
+          atomicAdd(&s_range[r * E + v[u]], 1);
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kLayoutThreads) {
+      const int before = s_range[e], mine = s_range[E + e];
+      const int rest = s_range[2 * E + e], after = s_range[3 * E + e];
+      s_off[e] = before + mine + rest + after;
+      s_pre[e] = before + mine;
+      if constexpr (kLists) {
+        s_bpre[e] = before;
+        s_bscan[e] = mine + rest;
+      }
+    }
+  } else if (!kSingle) {
     int parts = 1;
     while (nblocks >= 64 && parts * 2 * E <= kLayoutThreads && parts < kLayoutWaves) parts *= 2;
     const int me = static_cast<int>(blockIdx.x);
@@ -464,6 +513,17 @@ hipError_t launch_pass(const Buckets& b, const LayoutOut& o, hipStream_t stream)
       hipLaunchKernelGGL((layout_place_kernel<kRanks, kLayoutSingleSteps, true, false>), dim3(1),
                          dim3(kLayoutThreads), 0, stream, b, o);
     return hipGetLastError();
+  }
+  if constexpr (!kRanks) {
+    if (nblocks <= kLayoutFusedBlocks) {   // one launch: every workgroup counts all slots
+      if (o.block_chunks > 0)
+        hipLaunchKernelGGL((layout_place_kernel<false, kLayoutSteps, false, true, true>),
+                           dim3(nblocks), dim3(kLayoutThreads), 0, stream, b, o);
+      else
+        hipLaunchKernelGGL((layout_place_kernel<false, kLayoutSteps, false, false, true>),
+                           dim3(nblocks), dim3(kLayoutThreads), 0, stream, b, o);
+      return hipGetLastError();
+    }
   }
   hipLaunchKernelGGL(layout_hist_kernel<kRanks>, dim3(nblocks), dim3(kLayoutThreads), 0, stream,
                      b, o);

@@ -19,6 +19,15 @@ constexpr int kLayoutChunk = kLayoutThreads * kLayoutSteps;  // 1024 slots per w
 constexpr int kLayoutSingleSteps = 8;
 constexpr int kLayoutSingleChunk = kLayoutThreads * kLayoutSingleSteps;  // 4096 slots
 
+// Up to this many workgroups the expert layout is one launch in which each
+// workgroup counts every slot itself (no histogram kernel before it). Each
+// workgroup's count costs about 0.18 us per 1024-slot chunk (the rate of LDS
+// atomics on one compute unit), the second launch about 2-3 us, so one
+// launch pays up to here: top-8 of 256, same box, one launch / two, us:
+// 8 chunks 6.75 / 9.66, 16 chunks 8.26 / 8.44, 24 chunks (T=4096, top-6 of
+// 64) 9.15 / 9.66, 32 chunks 11.2 / 9.07, 64 chunks 17.2 / 10.2.
+constexpr int kLayoutFusedBlocks = 24;
+
 inline int layout_blocks(int64_t slots) {
   int64_t b = (slots + kLayoutChunk - 1) / kLayoutChunk;
   return b < 1 ? 1 : (int)b;

@@ -324,8 +324,8 @@ int moe_route(moe_handle_t h, const float* d_logits, int32_t num_tokens, int sco
  * token's rows from the ids themselves -- a row is the number of valid slots
  * with a smaller expert id plus the number of earlier slots with the same id.
  * That count grows with num_tokens^2: from 640 tokens on the call enqueues
- * the two layout kernels and the dispatch instead (same results, faster
- * there), and num_tokens must lie in [0, min(max_tokens,
+ * the layout of moe_dispatch_layout and the dispatch instead (same results,
+ * faster there), and num_tokens must lie in [0, min(max_tokens,
  * MOE_EP_LL_MAX_TOKENS)]. dtype, d_out, d_scales and out_rows as in
  * moe_dispatch. Leaves the handle's layout ready, as moe_dispatch_layout does:
  * moe_layout_view, moe_dispatch and moe_combine follow as usual. */

@@ -111,8 +111,9 @@ def test_handle_reused_across_forms():
 
 
 def test_layout_dispatch_call_uses_lists():
-    """moe_layout_dispatch from 640 tokens on runs the two layout launches and
-    then the dispatch; at 1024 tokens x top-8 that is the blocked form."""
+    """moe_layout_dispatch from 640 tokens on runs the layout of
+    moe_dispatch_layout (at 1024 tokens x top-8 one launch that also writes the
+    lists) and then the dispatch, here in the blocked form."""
     T, H, k, E, R = 1024, 7168, 8, 256, 8
     idx = ids(T, k, E, "invalid", seed=9)
     xb = bf16_rows(T, H, seed=10)
