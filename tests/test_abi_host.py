@@ -57,11 +57,13 @@ def test_workspace_bytes(lib):
     # expert layout: pos + src_idx + 32 histograms (one per 1024-slot workgroup) of 256
     # experts; rank layout: slot_row + rank_pos [T, 8] + src [T * 8] + 32 histograms of 8
     # ranks; decode-time layout: pos [1024 * 8] + counts [256]; blocked bf16 dispatch: (row,
-    # token) lists of (32 + 32 / 8 + 1) blocks' worth of 1024 entries + 32 list lengths;
-    # small arrays
+    # token) lists of (32 + 32 / 8 + 1) blocks' worth of 1024 entries, padded instead of
+    # carrying lengths; then the small arrays (status words, counts and offsets), every one
+    # of the 19 regions starting on a 256-byte boundary
     need = (2 * 4 * slots + 32 * 256 * 4 + 4 * slots + 4 * 4096 * 8 + 4 * 4096 * 8 + 32 * 8 * 4
-            + 4 * 1024 * 8 + 4 * 256 + 8 * (32 + 4 + 1) * 1024 + 4 * 32)
-    assert need <= n < need + 16 * 1024
+            + 4 * 1024 * 8 + 4 * 256 + 8 * (32 + 4 + 1) * 1024)
+    small = 3 * 4 * 4 + 4 * 256 + 4 * 257 + 2 * 4 * 8 + 2 * 4 * 9
+    assert need + small <= n <= need + small + 19 * 255
     assert n % 256 == 0
     zero = lib.moe_workspace_bytes(ctypes.byref(cfg(0)))
     assert zero > 0
