@@ -16,10 +16,14 @@
 // workgroup; the wavefront fetches the token's k row indices with scalar
 // loads, reads its slice of the token row once (16 bytes per lane) and
 // writes it to the k destination rows with 16-byte stores. Standard bf16:
-// one workgroup per item, the token's slots spread over its wavefronts
+// from kXcds layout chunks on (while a chunk's tokens hold at most
+// kBlockXBytes of x) the blocked form, whose wavefronts each copy one 1 KiB
+// slice of one row along the layout's block lists, the blocks of an XCD slot
+// one after another (dispatch_bf16_blocks_kernel); otherwise one workgroup
+// per item, the token's slots spread over its wavefronts
 // (dispatch_bf16_slots_kernel), or under a cap below kSlotsFormMinCap
 // workgroups the one-wavefront form. No two wavefronts write the same bytes:
-// no atomics, and no barrier in either form.
+// no atomics, and no barrier in any form.
 //
 // Row stores are non-temporal: each dispatched row is written once and its
 // next reader (the expert computation) is another kernel, so the rows stream

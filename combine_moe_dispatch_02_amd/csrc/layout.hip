@@ -594,6 +594,8 @@ hipError_t layout_scratch(int32_t** out) {
 size_t layout_scratch_ints(int num_tokens, int topk, int num_experts) {
   const int64_t slots = int64_t(num_tokens) * topk;
   if (slots <= kLayoutSingleChunk) return 0;   // one workgroup, no histograms
+  // one launch, every workgroup counting all slots itself: no histograms
+  if (layout_blocks(slots) <= kLayoutFusedBlocks) return 0;
   return static_cast<size_t>(layout_blocks(slots)) * static_cast<size_t>(num_experts);
 }
 

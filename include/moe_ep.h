@@ -158,8 +158,9 @@ int moe_layout_view(moe_handle_t h, moe_layout_view_t* out);
  * per-workgroup histograms go to a static device array of
  * MOE_EP_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends:
  * ceil(num_tokens * topk / 1024) * num_experts * 4 bytes must fit in it (e.g.
- * 2,097,152 slots at 256 experts; no histograms at all up to 4096 slots),
- * else MOE_ERR_UNSUPPORTED and nothing is enqueued. The configuration limits
+ * 2,097,152 slots at 256 experts; no histograms at all up to 24 * 1024
+ * slots, which are laid out in one launch), else MOE_ERR_UNSUPPORTED and
+ * nothing is enqueued. The configuration limits
  * are moe_handle_create's. Every call on one GPU shares that GPU's array, so
  * calls that may overlap on one GPU (other streams, other threads) race:
  * order them on one stream. The first call on each device looks the array up

@@ -12,8 +12,9 @@ chunks and one more, blocks whose edges split a token's slots, a row whose
 last slice holds one 16-byte vector, the narrowest row, every slot on one
 expert, invalid ids, k = 1 and k = 32, XCD slots that walk two and eight
 blocks, 128 layout workgroups (column sums split over threads) feeding blocks
-of 16 chunks, a handle reused across sizes that take different forms, and the
-one-call layout + dispatch.
+of 16 chunks, the one-launch layout feeding blocks of 2 chunks, a handle
+reused across sizes that take different forms, and the one-call layout +
+dispatch.
 """
 import numpy as np
 import pytest
@@ -68,6 +69,8 @@ CASES = [
     ("eight_blocks_per_slot", 65536, 1, 64, 8, 1032, "random"),
     # 128 chunks of 16 KiB: blocks of 16 chunks, the layout's split column sums
     ("split_sums_lists", 16384, 8, 128, 8, 64, "invalid"),
+    # 16 chunks, the last one partial: the one-launch layout, blocks of 2 chunks
+    ("one_launch_layout_pairs", 2000, 8, 256, 8, 64, "invalid"),
 ]
 
 

@@ -46,8 +46,8 @@ def _handle_layout(idx: np.ndarray, E: int, R: int) -> dict:
 def test_noalloc_layout_matches_workspace_layout(order):
     """Calls in a row on one GPU, each compared with the workspace layout
     entry by entry: the DeepSeek-V3-like batch (32 histogram workgroups), a
-    smaller one that still needs histograms, and one small enough for a
-    single workgroup (no histograms)."""
+    smaller one laid out in one launch (6 workgroups, each counting every
+    slot; no histograms), and one small enough for a single workgroup."""
     wl = make_workload("deepseekv3")
     rng = np.random.default_rng(3)
     small = np.stack([rng.permutation(64)[:6] for _ in range(1000)]).astype(np.int32)
