@@ -1,6 +1,7 @@
 """Exhaustive GPU check of the fp32 -> E4M3 conversion of the FP8 and MXFP8
 dispatch kernels (clamp to +-448, then the gfx950 conversion instruction,
-round to nearest even), over every finite fp32 bit pattern.
+round to nearest even), over every finite fp32 bit pattern; and of the FP8
+kernels' quotient x / scale, over every (amax, x) pair of bf16 values.
 
 The FP8 dispatch quantises x / scale in fp32 and converts that quotient
 ("MoE / Hybrid-EP Validation", "FP8 dispatch restriction": dispatch carries
@@ -42,7 +43,42 @@ def _lib():
     lib = ctypes.CDLL(LIB)
     lib.e4m3_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
     lib.e4m3_sweep.restype = ctypes.c_int
+    lib.e4m3_quotient_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.e4m3_quotient_sweep.restype = ctypes.c_int
     return lib
+
+
+def test_fp8_quotient_every_bf16_pair():
+    """The FP8 kernels form x / scale with e4m3_quotient (a reciprocal per
+    scale and Markstein's fma corrections) instead of an IEEE division; its
+    E4M3 code must be the IEEE quotient's for every input a block can hold:
+    every positive finite bf16 amax (scale = amax / 448) against every bf16 x
+    with |x| <= amax, and NaN x (2,139,029,504 pairs, about 1.76e9 of them on
+    the fast path)."""
+    lib = _lib()
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    counts = torch.zeros(3, dtype=torch.int32, device=dev)
+    example = torch.zeros(1, dtype=torch.int32, device=dev)
+    n_all, per_call = 0x7F7F, 4096
+    t0 = time.time()
+    for first in range(1, n_all + 1, per_call):
+        n = min(per_call, n_all + 1 - first)
+        rc = lib.e4m3_quotient_sweep(first, n, ctypes.c_void_p(counts.data_ptr()),
+                                     ctypes.c_void_p(example.data_ptr()),
+                                     ctypes.c_void_p(stream.cuda_stream))
+        assert rc == 0, f"e4m3_quotient_sweep returned {rc} at amax 0x{first:04x}"
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy().view(np.uint32)
+    ex = int(example.cpu().numpy().view(np.uint32)[0])
+    print(f"[quotient sweep] {time.time() - t0:.1f} s: {c[0]} in-domain and {c[1]} out-of-domain "
+          f"disagreements, {c[2]} pairs on the fast path", flush=True)
+    assert c[0] == 0, f"amax 0x{ex >> 16:04x}, x 0x{ex & 0xFFFF:04x}: codes differ"
+    # the fast path covered every scale of 2^-90 or more (host count, IEEE fp32 division)
+    amax = (np.arange(1, n_all + 1, dtype=np.uint32) << 16).view(np.float32)
+    scale = amax / np.float32(448.0)
+    assert int(c[2]) == int(np.count_nonzero(scale >= np.float32(2.0 ** -90))) * 65536
 
 
 def test_e4m3_conversion_every_finite_fp32():
