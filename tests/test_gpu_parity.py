@@ -228,8 +228,10 @@ def test_large_token_count_layout():
 
 # Slot counts at the layout's workgroup boundaries: one workgroup with 2, 4 or
 # 8 steps of 64 slots per wavefront up to 1024 / 2048 / 4096 slots, then
-# workgroups of 1024 slots (a ragged last one included).
-BOUNDARY_SLOTS = (1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097, 5120, 8191)
+# workgroups of 1024 slots (a ragged last one included), in one launch up to
+# 24 of them and in two (histograms, then placement) from 25 on.
+BOUNDARY_SLOTS = (1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097, 5120, 8191,
+                  24575, 24576, 24577)
 
 
 @pytest.mark.parametrize("slots", BOUNDARY_SLOTS)
