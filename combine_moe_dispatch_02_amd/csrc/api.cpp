@@ -440,13 +440,10 @@ int moe_dispatch_ranks(moe_handle_t h, const void* d_x, const int32_t* d_topk_id
       !aligned(d_recv_idx, 4) || !aligned(d_recv_w, 4))
     return fail(MOE_ERR_INVALID_ARG,
                 "moe_dispatch_ranks: x and out must be 16-byte aligned, the rest 4-byte aligned");
-  hipError_t err = moe::launch_dispatch_sparse(d_x, h->rank.slot_row, d_out, out_rows,
-                                               h->rank_num_tokens, h->cfg.topk, h->cfg.hidden,
-                                               h->max_workgroups, stream);
-  if (err == hipSuccess)
-    err = moe::launch_rank_meta(d_topk_idx, d_w, h->rank.slot_row, h->rank_num_tokens,
-                                h->cfg.topk, h->cfg.num_experts, h->cfg.num_ranks, out_rows,
-                                d_recv_idx, d_recv_w, stream);
+  const hipError_t err = moe::launch_dispatch_ranks(
+      d_x, h->rank.slot_row, d_out, out_rows, h->rank_num_tokens, h->cfg.topk, h->cfg.hidden,
+      h->max_workgroups, d_topk_idx, d_w, h->cfg.num_experts, h->cfg.num_ranks, d_recv_idx,
+      d_recv_w, stream);
   return hip_status(err, "moe_dispatch_ranks");
 }
 

@@ -349,9 +349,45 @@ __device__ __forceinline__ void payload_item(const u32x4* __restrict__ x, const 
 // payload functions above, which the decode-time kernel uses): with them
 // written out, hipcc keeps the contiguous-batch fast path for the row
 // indices, worth 1-2.5% here.
+// Receiver metadata of the rank-deduplicated exchange. For each (token,
+// rank) row p of token t (opened by slot jr: pos[t, jr] = p) and each slot j
+// of t, entry (p, j) says whether slot j's expert lives on that row's rank --
+// its local id e - r*E/R and its weight -- or not (-1 and 0).
+struct RankMeta {
+  const int32_t* idx;   // [T, k] expert ids
+  const float* w;       // [T, k] weights
+  int num_experts, per_rank;
+  int32_t* recv_idx;    // [rows, k]
+  float* recv_w;        // [rows, k]
+};
+
+// Token t's k x k metadata entries, spread over the wavefront's lanes (one
+// (row slot jr, slot j) pair per lane and step; consecutive lanes write
+// consecutive entries of a row).
+__device__ __forceinline__ void write_rank_meta(const RankMeta& m, const int32_t* __restrict__ pos,
+                                                int t, int topk, int64_t rows, int lane) {
+  const int base = t * topk;
+  for (int q = lane; q < topk * topk; q += 64) {
+    const int jr = q / topk, j = q - jr * topk;
+    const int p = pos[base + jr];
+    if (p < 0 || p >= rows) continue;
+    const int e = m.idx[base + j];
+    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(m.num_experts);
+    const int rr = m.idx[base + jr] / m.per_rank;   // the opening slot's expert is valid
+    const bool local = valid && e / m.per_rank == rr;
+    m.recv_idx[static_cast<size_t>(p) * topk + j] = local ? e - rr * m.per_rank : -1;
+    m.recv_w[static_cast<size_t>(p) * topk + j] = local ? m.w[base + j] : 0.0f;
+  }
+}
+
+// kMeta: the rank-deduplicated exchange, whose first-slice wavefront of each
+// token also writes the token's receiver metadata (a kernel of its own for
+// it took a 4.4 us launch of the 67 us call at T=4096, H=7168, k=8).
+template <bool kMeta>
 __global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, int topk, int64_t rows,
-    u32x4* __restrict__ out, int num_tokens, int nvec, int slices, int payload_blocks) {
+    u32x4* __restrict__ out, int num_tokens, int nvec, int slices, int payload_blocks,
+    RankMeta meta) {
   const int lane = threadIdx.x & 63;
   const int nitems = num_tokens * slices;
   for (int item = blockIdx.x * kItemWaves + wave_index(); item < nitems;
@@ -370,6 +406,8 @@ __global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_kernel(
       for (int jj = 0; jj < kSlotBatch; ++jj)
         if (p[jj] >= 0 && active) store_row(&out[static_cast<size_t>(p[jj]) * nvec + v], r);
     }
+    if constexpr (kMeta)
+      if (slice == 0) write_rank_meta(meta, pos, t, topk, rows, lane);
   }
 }
 
@@ -939,43 +977,7 @@ __global__ __launch_bounds__(64 * kFixedWaves) void dispatch_fused_kernel(
   }
 }
 
-// Receiver metadata of the rank-deduplicated exchange. One thread per slot
-// (t, j): for each (token, rank) row p of token t (opened by slot jr), entry
-// (p, j) says whether slot j's expert lives on that row's rank -- its local id
-// e - r*E/R and its weight -- or not (-1 and 0).
-__global__ __launch_bounds__(256) void rank_meta_kernel(
-    const int32_t* __restrict__ idx, const float* __restrict__ w,
-    const int32_t* __restrict__ slot_row, int num_tokens, int topk, int num_experts,
-    int per_rank, int64_t rows, int32_t* __restrict__ recv_idx, float* __restrict__ recv_w) {
-  const int slot = blockIdx.x * blockDim.x + threadIdx.x;
-  if (slot >= num_tokens * topk) return;
-  const int t = slot / topk, j = slot - t * topk;
-  const int e = idx[slot];
-  const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(num_experts);
-  const int r = valid ? e / per_rank : -1;
-  const float wj = w[slot];
-  for (int jr = 0; jr < topk; ++jr) {
-    const int p = slot_row[t * topk + jr];
-    if (p < 0 || p >= rows) continue;
-    const int rr = idx[t * topk + jr] / per_rank;   // the opening slot's expert is valid
-    const bool local = valid && r == rr;
-    recv_idx[static_cast<size_t>(p) * topk + j] = local ? e - rr * per_rank : -1;
-    recv_w[static_cast<size_t>(p) * topk + j] = local ? wj : 0.0f;
-  }
-}
-
 }  // namespace
-
-hipError_t launch_rank_meta(const int32_t* d_idx, const float* d_w, const int32_t* d_slot_row,
-                            int num_tokens, int topk, int num_experts, int num_ranks, int64_t rows,
-                            int32_t* d_recv_idx, float* d_recv_w, hipStream_t stream) {
-  if (num_tokens == 0) return hipSuccess;
-  const int slots = num_tokens * topk;
-  hipLaunchKernelGGL(rank_meta_kernel, dim3((slots + 255) / 256), dim3(256), 0, stream, d_idx, d_w,
-                     d_slot_row, num_tokens, topk, num_experts, num_experts / num_ranks, rows,
-                     d_recv_idx, d_recv_w);
-  return hipGetLastError();
-}
 
 hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, void* d_out,
                            void* d_scales, int64_t rows, int num_tokens, int topk, int hidden,
@@ -990,8 +992,8 @@ hipError_t launch_dispatch(int dtype, const void* d_x, const int32_t* d_pos, voi
       int64_t(max_blocks) * kItemWaves < int64_t(num_tokens) * slices) {
     // Capped below kSlotsFormMinCap workgroups: each wavefront takes one item
     // and all of its k slots.
-    hipLaunchKernelGGL(dispatch_bf16_kernel, grid, block, 0, stream, x, d_pos, topk, rows, out,
-                       num_tokens, hidden / 8, slices, payload);
+    hipLaunchKernelGGL(dispatch_bf16_kernel<false>, grid, block, 0, stream, x, d_pos, topk, rows,
+                       out, num_tokens, hidden / 8, slices, payload, RankMeta{});
   } else if (dtype == MOE_DTYPE_BF16) {
     // One workgroup of min(ceil(k / kSlotsPerWave), kSlotWaves) wavefronts
     // per item; a cap keeps the wavefront count of max_blocks workgroups of
@@ -1059,16 +1061,19 @@ hipError_t launch_dispatch_blocks(const void* d_x, const int2* d_order, void* d_
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_sparse(const void* d_x, const int32_t* d_pos, void* d_out, int64_t rows,
-                                  int num_tokens, int topk, int hidden, int max_blocks,
-                                  hipStream_t stream) {
+hipError_t launch_dispatch_ranks(const void* d_x, const int32_t* d_slot_row, void* d_out,
+                                 int64_t rows, int num_tokens, int topk, int hidden,
+                                 int max_blocks, const int32_t* d_idx, const float* d_w,
+                                 int num_experts, int num_ranks, int32_t* d_recv_idx,
+                                 float* d_recv_w, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int slices = (hidden / 8 + 63) / 64;
   const dim3 grid = item_grid(int64_t(num_tokens) * slices, max_blocks), block(64 * kItemWaves);
-  hipLaunchKernelGGL(dispatch_bf16_kernel, grid, block, 0, stream,
-                     static_cast<const u32x4*>(d_x), d_pos, topk, rows,
+  const RankMeta meta{d_idx, d_w, num_experts, num_experts / num_ranks, d_recv_idx, d_recv_w};
+  hipLaunchKernelGGL(dispatch_bf16_kernel<true>, grid, block, 0, stream,
+                     static_cast<const u32x4*>(d_x), d_slot_row, topk, rows,
                      static_cast<u32x4*>(d_out), num_tokens, hidden / 8, slices,
-                     static_cast<int>(grid.x));
+                     static_cast<int>(grid.x), meta);
   return hipGetLastError();
 }
 

@@ -180,12 +180,16 @@ hipError_t launch_dispatch_blocks(const void* d_x, const int2* d_order, void* d_
                                   int num_tokens, int topk, int hidden, int block_chunks,
                                   hipStream_t stream);
 
-// bf16 dispatch for tables in which many slots are -1 (the rank-deduplicated
-// layout): one wavefront per (token, slice) loops over the slots, where
-// launch_dispatch gives every slot a wavefront of its own.
-hipError_t launch_dispatch_sparse(const void* d_x, const int32_t* d_pos, void* d_out, int64_t rows,
-                                  int num_tokens, int topk, int hidden, int max_blocks,
-                                  hipStream_t stream);
+// bf16 dispatch of the rank-deduplicated layout, whose table has many -1
+// slots: one wavefront per (token, slice) loops over the slots (where
+// launch_dispatch gives every slot a wavefront of its own), and the
+// wavefronts of slice 0 also write the receiver metadata d_recv_idx /
+// d_recv_w [rows, topk] of the token's rows.
+hipError_t launch_dispatch_ranks(const void* d_x, const int32_t* d_slot_row, void* d_out,
+                                 int64_t rows, int num_tokens, int topk, int hidden,
+                                 int max_blocks, const int32_t* d_idx, const float* d_w,
+                                 int num_experts, int num_ranks, int32_t* d_recv_idx,
+                                 float* d_recv_w, hipStream_t stream);
 
 // Fixed-capacity (decode-time) layout and dispatch in one launch: rows
 // [e*capacity, (e+1)*capacity) belong to expert e. Records d_pos [T, k],
@@ -276,10 +280,6 @@ inline dim3 wave_grid(int64_t num_items, int waves, int max_blocks) {
   }
   return dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks));
 }
-
-hipError_t launch_rank_meta(const int32_t* d_idx, const float* d_w, const int32_t* d_slot_row,
-                            int num_tokens, int topk, int num_experts, int num_ranks, int64_t rows,
-                            int32_t* d_recv_idx, float* d_recv_w, hipStream_t stream);
 
 hipError_t launch_combine_ranks(const void* d_y, int64_t rows, const int32_t* d_rank_pos,
                                 void* d_out, int num_tokens, int num_ranks, int hidden,
