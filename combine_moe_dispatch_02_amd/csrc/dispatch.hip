@@ -522,7 +522,11 @@ __global__ __launch_bounds__(64 * kSlotWaves) void dispatch_bf16_slots_kernel(
 // Past that the scalar unit no longer bounds it (the address arithmetic
 // moved to the vector unit, 13 fewer scalar instructions, measured the same
 // 90.5 us). Correctness never depends on where a workgroup runs.
-constexpr int kBlockPrefetchItems = 1024;
+// How far ahead (in the slot's items) the first items prefetch: same-box
+// A/B, x from HBM, us at 256 / 512 / 1024 / 2048 items: T=4096, H=2048,
+// top-6 21.3 / 21.2 / 22.0 / 23.7; T=4096, H=7168, top-8 90.9 / 90.9 / 90.8 /
+// 91.8; T=16384, H=4096, Zipf routing 191 / 190.6 / 191.6 / 193.
+constexpr int kBlockPrefetchItems = 512;
 
 __global__ __launch_bounds__(64 * kItemWaves) void dispatch_bf16_blocks_kernel(
     const u32x4* __restrict__ x, const int2* __restrict__ order, u32x4* __restrict__ out,
