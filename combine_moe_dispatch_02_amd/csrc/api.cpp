@@ -313,8 +313,9 @@ int moe_dispatch_layout_noalloc(const int32_t* d_topk_idx, int32_t num_tokens, i
   int32_t* scratch = nullptr;
   hipError_t err = moe::layout_scratch(&scratch);
   if (err != hipSuccess) return hip_status(err, fn);
+  // no block lists: moe_dispatch never reads this layout
   const moe::LayoutArrays a{d_status, d_counts_e, d_offsets_e, d_counts_r, d_offsets_r,
-                            scratch,  d_pos,      d_src_idx};
+                            scratch,  d_pos,      d_src_idx,   nullptr};
   err = moe::launch_layout(d_topk_idx, num_tokens, topk, num_experts, num_ranks, a, stream);
   return hip_status(err, fn);
 }

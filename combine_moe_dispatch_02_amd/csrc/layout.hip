@@ -606,7 +606,7 @@ hipError_t launch_rank_layout(const int32_t* d_idx, int num_tokens, int topk, in
   Buckets b{d_idx, num_tokens * topk, topk, num_experts, rank_multiplier(per),
             num_ranks, bits_for(num_ranks), rows};
   LayoutOut o{a.hist, a.counts, a.offsets, nullptr, nullptr, a.slot_row, a.src,
-              a.status, a.rank_pos, num_ranks, per};
+              a.status, a.rank_pos, num_ranks, per, nullptr, 0};
   return launch_pass<true>(b, o, stream);
 }
 
