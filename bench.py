@@ -462,8 +462,8 @@ def main():
             context[label] = {"bytes": moved, "us_median": us,
                               "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
         del cbufs
-        # Context 4, same kernel and method: the bf16 dispatch with its
-        # destination rows in token order. When every slot of token t goes to
+        # Context 4, same kernels and method: the bf16 and FP8 dispatches with
+        # their destination rows in token order. When every slot of token t goes to
         # expert t*k / (T*k/E) (repeated ids are independent slots), the layout
         # puts slot (t, j) at row t*k + j: the same bytes as the workload's
         # routing, with the row writes sequential instead of spread over the E
@@ -479,6 +479,14 @@ def main():
                               args.sustained_iters)
             context["dispatch_bf16_rows_in_order"] = {
                 "us_median": us, **rate(nbytes["dispatch_bf16"], us),
+                "positions_in_order": in_order,
+                "routing": "every slot of token t on expert t*k/(T*k/E), not the workload's"}
+            # the FP8 dispatch under the same in-order layout (its own x copies)
+            us8 = sustained_us(lambda i: h.dispatch(B("xq", i), fp8=True, out=B("q_out", i),
+                                                    scales=B("q_scales", i)),
+                               args.sustained_iters)
+            context["dispatch_fp8_rows_in_order"] = {
+                "us_median": us8, **rate(nbytes["dispatch_fp8"], us8),
                 "positions_in_order": in_order,
                 "routing": "every slot of token t on expert t*k/(T*k/E), not the workload's"}
             h.layout(bufs["idx"][0])
