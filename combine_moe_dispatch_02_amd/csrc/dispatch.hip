@@ -17,7 +17,8 @@
 // loads, reads its slice of the token row once (16 bytes per lane) and
 // writes it to the k destination rows with 16-byte stores. Standard bf16:
 // from kXcds layout chunks on (while a chunk's tokens hold at most
-// kBlockXBytes of x) the blocked form, whose wavefronts each copy one 1 KiB
+// kBlockXBytes of x and the batch at most kBlockedMaxXBytes) the blocked
+// form, whose wavefronts each copy one 1 KiB
 // slice of one row along the layout's block lists, the blocks of an XCD slot
 // one after another (dispatch_bf16_blocks_kernel); otherwise one workgroup
 // per item, the token's slots spread over its wavefronts
@@ -1054,7 +1055,10 @@ hipError_t launch_dispatch_blocks(const void* d_x, const int2* d_order, void* d_
   const int tpb = bs / topk + 2;
   // Every index the kernel forms stays below 2^31 (fast_div's range).
   const int64_t slot_items = int64_t(per_slot) * bs * slices;
-  const int64_t prefetch_items = int64_t(per_slot) * tpb * slices;
+  // The early burst of x only while the batch's x leaves room in the
+  // last-level cache (kPrefetchMaxXBytes).
+  const int64_t prefetch_items =
+      int64_t(num_tokens) * 2 * hidden > kPrefetchMaxXBytes ? 0 : int64_t(per_slot) * tpb * slices;
   if (slot_items + kItemWaves > 0x7FFFFFFF || prefetch_items > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int64_t grid = (slot_items + kItemWaves - 1) / kItemWaves * kXcds;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;

@@ -78,10 +78,22 @@ constexpr int kXcds = MOE_EP_XCDS;
 // top-8 of 128, Zipf routing 203.4 / 194; T=4096, H=4096, 51.8 / 47.8).
 constexpr int64_t kBlockXBytes = int64_t(7) << 19;
 
+// The blocked form re-reads each token's x once per row from the cache
+// hierarchy, which holds while the batch's x fits well inside the 256 MB
+// last-level cache; its early burst of x only while x takes little more than
+// half of it. Same box, x from HBM, us, blocked with the burst / blocked
+// without it / per-slot form: T=8192, H=7168 (x 117 MB) 181 / 192 / 199;
+// T=16384, H=4096 (134 MB) 196-203 / 206-208 / 215 (with Zipf routing
+// 195-197 / 190-191 / 205); T=12288, H=7168 (176 MB) 369 / 287 / 302;
+// T=16384, H=7168 (235 MB) 480 / 419 / 393; T=32768, H=4096 (268 MB) 531 /
+// 467-472 / 437.
+constexpr int64_t kBlockedMaxXBytes = int64_t(192) << 20;
+constexpr int64_t kPrefetchMaxXBytes = int64_t(144) << 20;
+
 // Layout chunks per dispatch block for num_tokens x topk slots of `hidden`
 // bf16 channels, or 0 when the blocked form is not used: fewer than one block
-// per XCD slot, or one chunk's tokens already holding more than kBlockXBytes
-// of x. A power of two (the dispatch finds a row's block with a shift) with
+// per XCD slot, one chunk's tokens already holding more than kBlockXBytes of
+// x, or the batch's x more than kBlockedMaxXBytes. A power of two (the dispatch finds a row's block with a shift) with
 // at most kBlockXBytes of x and at most chunks / kXcds chunks, chosen so that
 // the busiest XCD slot gets as few chunks as possible (blocks b, b + 8, ...
 // share a slot: with 24 chunks, blocks of 2 would give four slots 4 chunks
@@ -90,6 +102,7 @@ inline int dispatch_block_chunks(int num_tokens, int topk, int hidden) {
   const int64_t slots = int64_t(num_tokens) * topk;
   const int64_t chunks = (slots + kLayoutChunk - 1) / kLayoutChunk;
   if (topk <= 0 || hidden <= 0 || chunks < kXcds) return 0;
+  if (int64_t(num_tokens) * 2 * hidden > kBlockedMaxXBytes) return 0;
   const int64_t chunk_x = int64_t(kLayoutChunk) * 2 * hidden / topk;
   if (chunk_x > kBlockXBytes) return 0;
   int64_t best = 1, best_load = (chunks + kXcds - 1) / kXcds;

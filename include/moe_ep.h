@@ -136,7 +136,8 @@ void moe_handle_destroy(moe_handle_t h);
  * `stream`; no host synchronisation. Marks the handle ready for dispatch and
  * combine with this num_tokens. For batches of at least 8 x 1024 slots whose
  * 1024-slot chunks each cover at most 3.5 MiB of x (1024 / topk tokens of
- * 2 * hidden bytes), it also writes, per block of consecutive slots, the
+ * 2 * hidden bytes) and whose x is at most 192 MiB (num_tokens * 2 * hidden
+ * bytes), it also writes, per block of consecutive slots, the
  * block's rows in ascending order (row, token), which the bf16 dispatch then
  * copies block by block, one XCD per block: the same rows, written one run per
  * expert at a time. */

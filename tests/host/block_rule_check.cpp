@@ -57,6 +57,7 @@ void check_block_rule() {
         const int64_t bs = int64_t(m) * moe::kLayoutChunk;
         const int64_t chunk_x = int64_t(moe::kLayoutChunk) * 2 * hidden / k;
         if (m * chunk_x > moe::kBlockXBytes) fail("block x above the limit", T, k, m);
+        if (int64_t(T) * 2 * hidden > moe::kBlockedMaxXBytes) fail("batch x above the limit", T, k, m);
         const int64_t nblocks = (chunks + m - 1) / m;
         const int64_t per_slot = (nblocks + moe::kXcds - 1) / moe::kXcds;
         const int64_t tpb = bs / k + 2;
@@ -76,6 +77,10 @@ void check_block_rule() {
   if (moe::dispatch_block_chunks(4096, 8, 7168) != 2) fail("V3-like rule", 4096, 8, 7168);
   if (moe::dispatch_block_chunks(4096, 6, 2048) != 1) fail("16B-like rule", 4096, 6, 2048);
   if (moe::dispatch_block_chunks(16384, 8, 4096) != 2) fail("Qwen3-like rule", 16384, 8, 4096);
+  if (moe::dispatch_block_chunks(12288, 8, 7168) != 2) fail("x of 176 MB", 12288, 8, 7168);
+  // the batch's x above 192 MiB: the per-slot form
+  if (moe::dispatch_block_chunks(16384, 8, 7168) != 0) fail("x of 235 MB", 16384, 8, 7168);
+  if (moe::dispatch_block_chunks(32768, 8, 4096) != 0) fail("x of 268 MB", 32768, 8, 4096);
   if (moe::dispatch_block_chunks(4096, 8, 4096) != 2) fail("H=4096 rule", 4096, 8, 4096);
   if (moe::dispatch_block_chunks(16384, 6, 2048) != 4) fail("16B-like rule, long batch", 16384, 6, 2048);
   // one chunk's tokens above 7/8 of an L2: the per-slot form
