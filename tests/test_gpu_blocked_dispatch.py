@@ -12,9 +12,10 @@ chunks and one more, blocks whose edges split a token's slots, a row whose
 last slice holds one 16-byte vector, the narrowest row, every slot on one
 expert, invalid ids, k = 1 and k = 32, XCD slots that walk two and eight
 blocks, 128 layout workgroups (column sums split over threads) feeding blocks
-of 16 chunks, the one-launch layout feeding blocks of 2 chunks, a handle
-reused across sizes that take different forms, and the one-call layout +
-dispatch.
+of 16 chunks, the one-launch layout feeding blocks of 2 chunks, a batch
+whose x is too large for the early burst and one too large for the blocked
+form, a handle reused across sizes that take different forms, and the
+one-call layout + dispatch.
 """
 import numpy as np
 import pytest
@@ -71,6 +72,10 @@ CASES = [
     ("split_sums_lists", 16384, 8, 128, 8, 64, "invalid"),
     # 16 chunks, the last one partial: the one-launch layout, blocks of 2 chunks
     ("one_launch_layout_pairs", 2000, 8, 256, 8, 64, "invalid"),
+    # x of 161 MB (above 144 MiB): blocked, without the early burst of x
+    ("blocked_without_burst", 45000, 1, 64, 8, 1792, "random"),
+    # x of 215 MB (above 192 MiB): the per-slot form, though 59 chunks
+    ("x_above_blocked_limit", 60000, 1, 64, 8, 1792, "random"),
 ]
 
 
