@@ -58,8 +58,11 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], bool use, float w, c
 
 // kWeighted = false sums the rows unweighted (weight 1, w unused): the final
 // reduction of the rank-deduplicated exchange, over the per-rank partial rows
-// of each token in ascending rank order.
-template <bool kWeighted>
+// of each token in ascending rank order. kBatch: rows loaded together (8, or
+// the power of two that covers a smaller topk, so that no load is issued for
+// slots past topk: at top-2 the 8-row batch repeated the last row six times
+// and ran at 46% of 8 TB/s).
+template <bool kWeighted, int kBatch>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(
     const u32x4* __restrict__ y, const float* __restrict__ w, const int32_t* __restrict__ pos,
     u32x4* __restrict__ out, int num_tokens, int topk, int nvec, int slices, int64_t rows) {
@@ -78,38 +81,38 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(
     const int32_t* pt = pos + static_cast<size_t>(t) * topk;
     const float* wt = kWeighted ? w + static_cast<size_t>(t) * topk : nullptr;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < topk; j0 += kSlotBatch) {
-      int p[kSlotBatch];
-      float wj[kSlotBatch];
-      bool use[kSlotBatch];
-      if (j0 + kSlotBatch <= topk) {   // full batch: contiguous, merges into wide scalar loads
+    for (int j0 = 0; j0 < topk; j0 += kBatch) {
+      int p[kBatch];
+      float wj[kBatch];
+      bool use[kBatch];
+      if (j0 + kBatch <= topk) {   // full batch: contiguous, merges into wide scalar loads
 #pragma unroll
-        for (int jj = 0; jj < kSlotBatch; ++jj) {
+        for (int jj = 0; jj < kBatch; ++jj) {
           p[jj] = pt[j0 + jj];
           wj[jj] = kWeighted ? wt[j0 + jj] : 1.0f;
         }
       } else {
 #pragma unroll
-        for (int jj = 0; jj < kSlotBatch; ++jj) {
+        for (int jj = 0; jj < kBatch; ++jj) {
           const int j = j0 + jj < topk ? j0 + jj : topk - 1;
           p[jj] = pt[j];
           wj[jj] = kWeighted ? wt[j] : 1.0f;
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < kSlotBatch; ++jj) {
+      for (int jj = 0; jj < kBatch; ++jj) {
         const bool row_ok = p[jj] >= 0 && p[jj] < rows;
         use[jj] = j0 + jj < topk && row_ok;
         p[jj] = row_ok ? p[jj] : 0;
       }
-      u32x4 r[kSlotBatch];
+      u32x4 r[kBatch];
 #pragma unroll
-      for (int jj = 0; jj < kSlotBatch; ++jj)
+      for (int jj = 0; jj < kBatch; ++jj)
         r[jj] = __builtin_nontemporal_load(&y[static_cast<size_t>(p[jj]) * nvec + vc]);
       // Unused slots leave acc untouched; selecting instead of branching keeps
       // the loads above in one batch.
 #pragma unroll
-      for (int jj = 0; jj < kSlotBatch; ++jj) accumulate(acc, use[jj], wj[jj], r[jj]);
+      for (int jj = 0; jj < kBatch; ++jj) accumulate(acc, use[jj], wj[jj], r[jj]);
     }
     if (active) {
       u32x4 o;
@@ -130,10 +133,19 @@ hipError_t launch_combine(const void* d_y, int64_t rows, const float* d_w, const
   if (num_tokens == 0) return hipSuccess;
   const int nvec = hidden / 8;
   const int slices = (nvec + 63) / 64;
-  hipLaunchKernelGGL(combine_kernel<true>,
-                     wave_grid(int64_t(num_tokens) * slices, kCombineWaves, max_blocks),
-                     dim3(64 * kCombineWaves), 0, stream, static_cast<const u32x4*>(d_y), d_w,
-                     d_pos, static_cast<u32x4*>(d_out), num_tokens, topk, nvec, slices, rows);
+  const dim3 grid = wave_grid(int64_t(num_tokens) * slices, kCombineWaves, max_blocks);
+  const dim3 block(64 * kCombineWaves);
+  const u32x4* y = static_cast<const u32x4*>(d_y);
+  u32x4* out = static_cast<u32x4*>(d_out);
+  if (topk <= 2)
+    hipLaunchKernelGGL((combine_kernel<true, 2>), grid, block, 0, stream, y, d_w, d_pos, out,
+                       num_tokens, topk, nvec, slices, rows);
+  else if (topk <= 4)
+    hipLaunchKernelGGL((combine_kernel<true, 4>), grid, block, 0, stream, y, d_w, d_pos, out,
+                       num_tokens, topk, nvec, slices, rows);
+  else
+    hipLaunchKernelGGL((combine_kernel<true, kSlotBatch>), grid, block, 0, stream, y, d_w, d_pos,
+                       out, num_tokens, topk, nvec, slices, rows);
   return hipGetLastError();
 }
 
@@ -143,7 +155,7 @@ hipError_t launch_combine_ranks(const void* d_y, int64_t rows, const int32_t* d_
   if (num_tokens == 0) return hipSuccess;
   const int nvec = hidden / 8;
   const int slices = (nvec + 63) / 64;
-  hipLaunchKernelGGL(combine_kernel<false>,
+  hipLaunchKernelGGL((combine_kernel<false, kSlotBatch>),
                      wave_grid(int64_t(num_tokens) * slices, kCombineWaves, max_blocks),
                      dim3(64 * kCombineWaves), 0, stream, static_cast<const u32x4*>(d_y), nullptr,
                      d_rank_pos, static_cast<u32x4*>(d_out), num_tokens, num_ranks, nvec, slices,
