@@ -133,7 +133,7 @@ def queue_ahead():
 
 
 KERNEL_OF_OP = {"dispatch_bf16": "dispatch_bf16_blocks_kernel",
-                "dispatch_fp8": "dispatch_fp8_kernel", "combine": "combine_kernel<true>"}
+                "dispatch_fp8": "dispatch_fp8_kernel", "combine": "combine_kernel<true, 8>"}
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "traffic_deepseekv3.json")
 
