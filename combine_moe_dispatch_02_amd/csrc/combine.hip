@@ -155,11 +155,24 @@ hipError_t launch_combine_ranks(const void* d_y, int64_t rows, const int32_t* d_
   if (num_tokens == 0) return hipSuccess;
   const int nvec = hidden / 8;
   const int slices = (nvec + 63) / 64;
-  hipLaunchKernelGGL((combine_kernel<false, kSlotBatch>),
-                     wave_grid(int64_t(num_tokens) * slices, kCombineWaves, max_blocks),
-                     dim3(64 * kCombineWaves), 0, stream, static_cast<const u32x4*>(d_y), nullptr,
-                     d_rank_pos, static_cast<u32x4*>(d_out), num_tokens, num_ranks, nvec, slices,
-                     rows);
+  const dim3 grid = wave_grid(int64_t(num_tokens) * slices, kCombineWaves, max_blocks);
+  const dim3 block(64 * kCombineWaves);
+  const u32x4* y = static_cast<const u32x4*>(d_y);
+  u32x4* out = static_cast<u32x4*>(d_out);
+  // The rows of one token are its R per-rank partial sums: the same batch
+  // sizes as the weighted combine, by R. Same-box A/B at T=4096, H=7168,
+  // top-8 of 256, us, 8-row batch against the matched one: R=2 44.6 -> 30.3,
+  // R=4 51.2 -> 44.9, R=8 unchanged (59.5); T=8192, H=4096, top-2 of 8, R=2
+  // 49.2 -> 29.5.
+  if (num_ranks <= 2)
+    hipLaunchKernelGGL((combine_kernel<false, 2>), grid, block, 0, stream, y, nullptr, d_rank_pos,
+                       out, num_tokens, num_ranks, nvec, slices, rows);
+  else if (num_ranks <= 4)
+    hipLaunchKernelGGL((combine_kernel<false, 4>), grid, block, 0, stream, y, nullptr, d_rank_pos,
+                       out, num_tokens, num_ranks, nvec, slices, rows);
+  else
+    hipLaunchKernelGGL((combine_kernel<false, kSlotBatch>), grid, block, 0, stream, y, nullptr,
+                       d_rank_pos, out, num_tokens, num_ranks, nvec, slices, rows);
   return hipGetLastError();
 }
 
